@@ -1,0 +1,151 @@
+// C entry points: argument checks, the gfx950 device check, then the launch.
+// Nothing here allocates, synchronises or reads device memory.
+#include <atomic>
+#include <cstring>
+
+#include "internal.h"
+#include "moe_route.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// The kernels are written for gfx950 only; any other device is rejected
+// rather than run on code built for another target.
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ERR_UNSUPPORTED_DEVICE;
+  int state = dev < kMaxDevices ? g_device_ok[dev].load(std::memory_order_relaxed) : 0;
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    state = 2;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess) {
+      const char* a = prop.gcnArchName;
+      if (std::strncmp(a, "gfx950", 6) == 0 && (a[6] == '\0' || a[6] == ':')) state = 1;
+    }
+    if (dev < kMaxDevices) g_device_ok[dev].store(state, std::memory_order_relaxed);
+  }
+  return state == 1 ? MOE_OK : MOE_ERR_UNSUPPORTED_DEVICE;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+bool slots_ok(int64_t n_rows, int32_t top_k) {
+  if (n_rows < 0 || top_k < 1 || top_k > MOE_MAX_TOP_K) return false;
+  return n_rows <= int64_t(0xFFFFFFFEu) / top_k;  // every slot index and position < sentinel
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_error_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_UNSUPPORTED_DEVICE: return "unsupported device (gfx950 required)";
+    case MOE_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_mask_padding(int32_t* routing_map, int64_t n_rows, int32_t top_k,
+                     const int32_t* real_token_count, int32_t tp_rank, void* stream) {
+  if (!slots_ok(n_rows, top_k) || tp_rank < 0 || real_token_count == nullptr ||
+      !aligned(real_token_count, 4))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (n_rows > 0 && (routing_map == nullptr || !aligned(routing_map, 4)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (const int d = check_device()) return d;
+  return launched(moe::launch_mask_padding(routing_map, n_rows, top_k, real_token_count, tp_rank,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_create_indices_workspace_bytes(int64_t n_slots, int32_t n_experts) {
+  if (n_slots < 0 || n_slots > int64_t(0xFFFFFFFEu) || n_experts < 1 || n_experts > MOE_MAX_EXPERTS)
+    return 0;
+  return moe::index_workspace_bytes(n_slots, n_experts);
+}
+
+int moe_create_indices(const int32_t* topk_ids, int64_t n_slots, int32_t n_experts,
+                       uint32_t* token_expert_order, uint32_t* expert_start_indices,
+                       uint32_t* restore_token_order, int32_t* expert_ids,
+                       uint32_t* expert_usage_stats, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (n_slots < 0 || n_slots > int64_t(0xFFFFFFFEu) || n_experts < 1 || n_experts > MOE_MAX_EXPERTS)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (expert_start_indices == nullptr || expert_ids == nullptr || expert_usage_stats == nullptr ||
+      workspace == nullptr)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (n_slots > 0 && (topk_ids == nullptr || token_expert_order == nullptr ||
+                      restore_token_order == nullptr))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(topk_ids, 4) || !aligned(token_expert_order, 4) || !aligned(expert_start_indices, 4) ||
+      !aligned(restore_token_order, 4) || !aligned(expert_ids, 4) ||
+      !aligned(expert_usage_stats, 4) || !aligned(workspace, 256))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < moe::index_workspace_bytes(n_slots, n_experts))
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (const int d = check_device()) return d;
+  return launched(moe::launch_create_indices(topk_ids, n_slots, n_experts, token_expert_order,
+                                             expert_start_indices, restore_token_order, expert_ids,
+                                             expert_usage_stats, workspace,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int moe_dispatch(const uint16_t* input_tokens, int64_t n_rows, int32_t hidden, int32_t top_k,
+                 const uint32_t* restore_token_order, uint16_t* out, int64_t out_rows,
+                 void* stream) {
+  if (!slots_ok(n_rows, top_k) || hidden <= 0 || hidden % 8 != 0 || out_rows < 0)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (n_rows > 0 && (input_tokens == nullptr || restore_token_order == nullptr))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (out_rows > 0 && out == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(input_tokens, 16) || !aligned(out, 16) || !aligned(restore_token_order, 4))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (const int d = check_device()) return d;
+  return launched(moe::launch_dispatch_bf16(input_tokens, n_rows, hidden, top_k,
+                                            restore_token_order, out, out_rows,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int moe_dispatch_mxfp4(const uint16_t* input_tokens, int64_t n_rows, int32_t hidden,
+                       int32_t top_k, const uint32_t* restore_token_order, uint8_t* out_q,
+                       uint8_t* out_scales, int64_t out_rows, uint32_t flags, void* stream) {
+  if (!slots_ok(n_rows, top_k) || hidden <= 0 || hidden % MOE_MXFP4_BLOCK != 0 || out_rows < 0 ||
+      flags != 0)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (n_rows > 0 && (input_tokens == nullptr || restore_token_order == nullptr))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (out_rows > 0 && (out_q == nullptr || out_scales == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(input_tokens, 16) || !aligned(out_q, 16) || !aligned(restore_token_order, 4))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (const int d = check_device()) return d;
+  return launched(moe::launch_dispatch_mxfp4(input_tokens, n_rows, hidden, top_k,
+                                             restore_token_order, out_q, out_scales, out_rows,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int moe_combine(const uint16_t* y, int64_t y_rows, const float* router_weights,
+                const uint32_t* restore_token_order, int64_t n_rows, int32_t hidden,
+                int32_t top_k, uint16_t* output_tokens, void* stream) {
+  if (!slots_ok(n_rows, top_k) || hidden <= 0 || hidden % 8 != 0 || y_rows < 0)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (n_rows > 0 && (router_weights == nullptr || restore_token_order == nullptr ||
+                     output_tokens == nullptr))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (y_rows > 0 && y == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(y, 16) || !aligned(output_tokens, 16) || !aligned(router_weights, 4) ||
+      !aligned(restore_token_order, 4))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (const int d = check_device()) return d;
+  return launched(moe::launch_combine(y, y_rows, router_weights, restore_token_order, n_rows,
+                                      hidden, top_k, output_tokens,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,150 @@
+// Stage 3: dispatch token rows into the expert-contiguous buffer, as bf16 or
+// as MXFP4 ("Struct_ep_dispatch_async_mxfp4": input_tokens [num_tokens,
+// hidden_size] go to the experts of topk_ids; FP4 quants travel with their
+// scales).  Token-major: one workgroup per token reads the row once and
+// writes it to each of its routed positions, so x is read once per token
+// instead of once per slot.
+#include "common.h"
+#include "internal.h"
+#include "rows.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kLoadsInFlight = 4;  // 16-byte vectors each lane loads before storing
+
+// E8M0 exponent of a 32-element block from the largest magnitude, given as
+// the 15-bit magnitude of a bf16 pattern: floor(log2 amax) - 2, clamped to
+// [-127, 127]; -127 for an all-zero block.
+__device__ __forceinline__ int mx_scale_exponent(uint32_t amax) {
+  if (amax == 0) return -127;
+  const int ef = int(amax >> 7);
+  const int fl = ef > 0 ? ef - 127 : -133 + (31 - __clz(amax));  // subnormal: m * 2^-133
+  const int se = fl - 2;
+  return se < -127 ? -127 : se;
+}
+
+// E2M1 nibble of one bf16 element for a block scaled by mul = 2^-se.
+// a = |x| * 2^-se is exact whenever it is >= 2^-126, and smaller values
+// round to code 0 either way.  On [0,2) the E2M1 grid has step 0.5, on
+// [2,4) step 1, on [4,8) step 2 (6 is the last code): rounding a / step to
+// an integer with ties to even is the nearest code, ties to the even code.
+__device__ __forceinline__ uint32_t e2m1_nibble(uint32_t bits, float mul) {
+  const float a = __uint_as_float((bits & 0x7FFFu) << 16) * mul;
+  float r;
+  uint32_t base;
+  if (a < 2.0f) {
+    r = __builtin_rintf(a * 2.0f);
+    base = 0;
+  } else if (a < 4.0f) {
+    r = __builtin_rintf(a);
+    base = 2;
+  } else {
+    r = __builtin_rintf(a * 0.5f);
+    base = 4;
+  }
+  uint32_t c = uint32_t(r) + base;
+  c = c > 7u ? 7u : c;
+  return c | ((bits >> 12) & 8u);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kRowThreads) void k_dispatch_bf16(
+    const u32x4* __restrict__ x, int64_t n_rows, int h16, int top_k, const uint32_t* __restrict__ restore,
+    u32x4* __restrict__ out, uint32_t limit) {
+  __shared__ uint32_t s_pos[kMaxTopK];
+  __shared__ int s_n;
+  for (int64_t t = blockIdx.x; t < n_rows; t += gridDim.x) {
+  const int n = gather_routed(restore, nullptr, t, top_k, limit, s_pos, nullptr, &s_n);
+  const u32x4* src = x + t * h16;
+  for (int c0 = threadIdx.x; n > 0 && c0 < h16; c0 += kRowThreads * kLoadsInFlight) {
+    u32x4 v[kLoadsInFlight];
+#pragma unroll
+    for (int u = 0; u < kLoadsInFlight; ++u) {
+      const int c = c0 + u * kRowThreads;
+      if (c < h16) v[u] = __builtin_nontemporal_load(src + c);
+    }
+    for (int j = 0; j < n; ++j) {
+      u32x4* dst = out + int64_t(s_pos[j]) * h16;
+#pragma unroll
+      for (int u = 0; u < kLoadsInFlight; ++u) {
+        const int c = c0 + u * kRowThreads;
+        if (c < h16) __builtin_nontemporal_store(v[u], dst + c);
+      }
+    }
+  }
+  __syncthreads();  // s_pos is rewritten for the next token
+  }
+}
+
+// One lane per 32-element block: 4 x 16-byte loads, 16 bytes of payload and
+// one scale byte per routed position.
+__global__ __launch_bounds__(kRowThreads) void k_dispatch_mxfp4(
+    const u32x4* __restrict__ x, int64_t n_rows, int h16, int top_k, const uint32_t* __restrict__ restore,
+    u32x4* __restrict__ q, uint8_t* __restrict__ scales, uint32_t limit) {
+  __shared__ uint32_t s_pos[kMaxTopK];
+  __shared__ int s_n;
+  const int nblk = h16 / 4;
+  for (int64_t t = blockIdx.x; t < n_rows; t += gridDim.x) {
+  const int n = gather_routed(restore, nullptr, t, top_k, limit, s_pos, nullptr, &s_n);
+  const u32x4* src = x + t * h16;
+  for (int b = threadIdx.x; n > 0 && b < nblk; b += kRowThreads) {
+    uint32_t w[16];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const u32x4 v = __builtin_nontemporal_load(src + 4 * b + u);
+      w[4 * u + 0] = v.x;
+      w[4 * u + 1] = v.y;
+      w[4 * u + 2] = v.z;
+      w[4 * u + 3] = v.w;
+    }
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = max(amax, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+    const int se = mx_scale_exponent(amax);
+    const float mul = __uint_as_float(uint32_t(127 - se) << 23);
+    uint32_t packed[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t byte = e2m1_nibble(w[i] & 0xFFFFu, mul) | (e2m1_nibble(w[i] >> 16, mul) << 4);
+      packed[i / 4] |= byte << (8 * (i % 4));
+    }
+    u32x4 pv;
+    pv.x = packed[0];
+    pv.y = packed[1];
+    pv.z = packed[2];
+    pv.w = packed[3];
+    const uint8_t sbyte = uint8_t(se + 127);
+    for (int j = 0; j < n; ++j) {
+      const int64_t p = s_pos[j];
+      __builtin_nontemporal_store(pv, q + p * nblk + b);
+      scales[p * nblk + b] = sbyte;
+    }
+  }
+  __syncthreads();  // s_pos is rewritten for the next token
+  }
+}
+
+hipError_t launch_dispatch_bf16(const uint16_t* x, int64_t n_rows, int hidden, int top_k,
+                                const uint32_t* restore, uint16_t* out, int64_t out_rows,
+                                hipStream_t s) {
+  if (n_rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_dispatch_bf16, dim3(row_grid(n_rows)), dim3(kRowThreads), 0, s,
+                     reinterpret_cast<const u32x4*>(x), n_rows, hidden / 8, top_k, restore,
+                     reinterpret_cast<u32x4*>(out), position_limit(out_rows));
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_mxfp4(const uint16_t* x, int64_t n_rows, int hidden, int top_k,
+                                 const uint32_t* restore, uint8_t* q, uint8_t* scales,
+                                 int64_t out_rows, hipStream_t s) {
+  if (n_rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_dispatch_mxfp4, dim3(row_grid(n_rows)), dim3(kRowThreads), 0, s,
+                     reinterpret_cast<const u32x4*>(x), n_rows, hidden / 8, top_k, restore,
+                     reinterpret_cast<u32x4*>(q), scales, position_limit(out_rows));
+  return hipGetLastError();
+}
+
+}  // namespace moe

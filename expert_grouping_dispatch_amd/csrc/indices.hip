@@ -1,0 +1,341 @@
+// Stage 2: expert-grouped indices ("moe_create_indices": histogram the expert
+// ids, scan the histogram into CSR offsets, scatter the slots).
+//
+// The pages' kernel is one CTA.  Here the slots are cut into chunks of
+// kIdxChunk; for S <= kIdxChunk one workgroup still does all three steps in
+// one launch, otherwise:
+//   k_index_zero     clears the lookback words and the chunk ticket;
+//   k_index_hist     per chunk: LDS histogram (wave-aggregated increments),
+//                    then a decoupled lookback over earlier chunks gives, per
+//                    bucket, the number of slots in all earlier chunks; the
+//                    chunk holding the last ticket also has the totals and
+//                    writes the CSR / active-expert / stats outputs;
+//   k_index_scatter  per chunk: stable ranks (wave ballots + per-wave LDS
+//                    counters) -> token_expert_order and restore_token_order.
+// Bucket b < E is expert b; bucket E collects the unrouted slots, which land
+// after every routed slot and fill token_expert_order[V, S) with sentinels.
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr uint64_t kFlagAggregate = uint64_t(1) << 32;  // count of this chunk only
+constexpr uint64_t kFlagPrefix = uint64_t(2) << 32;     // count of chunks [0, c]
+constexpr uint64_t kFlagStatusMask = ~uint64_t(0xFFFFFFFFu);
+constexpr uint32_t kSpinLimit = 1u << 20;
+constexpr int kLookbackWindow = 8;
+
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+__device__ __forceinline__ uint32_t bucket_of(int32_t id, uint32_t n_experts) {
+  return uint32_t(id) < n_experts ? uint32_t(id) : n_experts;
+}
+
+__device__ __forceinline__ bool is_leader(uint64_t peers) {
+  return peers != 0 && __builtin_ctzll(peers) == __lane_id();
+}
+
+// Count the chunk's slots per bucket into hist[0..E] (LDS, zeroed by caller).
+__device__ void chunk_histogram(const int32_t* __restrict__ ids, int64_t n_slots, int64_t begin,
+                                uint32_t n_experts, int nbits, uint32_t* hist) {
+  const int tid = threadIdx.x;
+  uint32_t key[kIdxRounds];
+  bool valid[kIdxRounds];
+#pragma unroll
+  for (int r = 0; r < kIdxRounds; ++r) {
+    const int64_t i = begin + int64_t(r) * kIdxThreads + tid;
+    valid[r] = i < n_slots;
+    key[r] = valid[r] ? bucket_of(ids[i], n_experts) : 0u;
+  }
+#pragma unroll
+  for (int r = 0; r < kIdxRounds; ++r) {
+    const uint64_t peers = match_peers(key[r], nbits, valid[r]);
+    if (valid[r] && is_leader(peers)) atomicAdd(&hist[key[r]], uint32_t(__popcll(peers)));
+  }
+}
+
+// Stable scatter of one chunk.  off[b] (LDS) = position of the chunk's first
+// slot of bucket b.  whist is LDS scratch [kIdxWaves][E+1].  Wave w owns the
+// kIdxRounds*64 consecutive slots starting at begin + w*kIdxRounds*64, so the
+// slot order is wave-major, round, lane -- ascending slot index.
+__device__ void chunk_scatter(const int32_t* __restrict__ ids, int64_t n_slots, int64_t begin,
+                              uint32_t n_experts, int nbits, const uint32_t* off, uint32_t* whist,
+                              uint32_t* __restrict__ teo, uint32_t* __restrict__ restore) {
+  const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
+  const int nb = int(n_experts) + 1;
+  uint32_t* my = whist + wave * nb;
+  const int64_t wbegin = begin + int64_t(wave) * kIdxRounds * kWave;
+
+  uint32_t key[kIdxRounds];
+  bool valid[kIdxRounds];
+  uint64_t peers[kIdxRounds];
+#pragma unroll
+  for (int r = 0; r < kIdxRounds; ++r) {
+    const int64_t i = wbegin + r * kWave + lane;
+    valid[r] = i < n_slots;
+    key[r] = valid[r] ? bucket_of(ids[i], n_experts) : 0u;
+  }
+  for (int b = lane; b < nb; b += kWave) my[b] = 0;
+  // pass 1: per-wave bucket counts (only this wave touches its row)
+#pragma unroll
+  for (int r = 0; r < kIdxRounds; ++r) {
+    peers[r] = match_peers(key[r], nbits, valid[r]);
+    if (valid[r] && is_leader(peers[r])) my[key[r]] += uint32_t(__popcll(peers[r]));
+  }
+  __syncthreads();
+  // exclusive prefix over waves, seeded with the chunk's bucket start
+  for (int b = tid; b < nb; b += kIdxThreads) {
+    uint32_t run = off[b];
+    for (int w = 0; w < kIdxWaves; ++w) {
+      const uint32_t c = whist[w * nb + b];
+      whist[w * nb + b] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  // pass 2: position = wave's running start of the bucket + rank among lower lanes
+  const uint64_t below = lanes_below();
+#pragma unroll
+  for (int r = 0; r < kIdxRounds; ++r) {
+    uint32_t pos = 0;
+    if (valid[r]) pos = my[key[r]] + uint32_t(__popcll(peers[r] & below));
+    if (valid[r] && is_leader(peers[r])) my[key[r]] += uint32_t(__popcll(peers[r]));
+    if (valid[r]) {
+      const uint32_t i = uint32_t(wbegin + r * kWave + lane);
+      const bool routed = key[r] < n_experts;
+      restore[i] = routed ? pos : kSent;
+      teo[pos] = routed ? i : kSent;
+    }
+  }
+}
+
+// Block-wide: from per-bucket totals tot[0..E] (LDS) write the bucket starts
+// base[0..E] (exclusive scan, base[E] = V) and the compacted CSR outputs.
+__device__ void finalize_counts(const uint32_t* tot, uint32_t n_experts, uint32_t* base,
+                                uint32_t* __restrict__ esi, int32_t* __restrict__ expert_ids,
+                                uint32_t* __restrict__ stats) {
+  __shared__ uint32_t part[3 * kIdxWaves];
+  const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
+  const int nb = int(n_experts) + 1;
+  const int ipt = (nb + kIdxThreads - 1) / kIdxThreads;
+  const int b0 = tid * ipt;
+  uint32_t s_tot = 0, s_act = 0, s_max = 0;
+  for (int q = 0; q < ipt; ++q) {
+    const int b = b0 + q;
+    if (b < nb) {
+      const uint32_t v = tot[b];
+      s_tot += v;
+      if (b < int(n_experts)) {
+        s_act += v > 0 ? 1u : 0u;
+        s_max = max(s_max, v);
+      }
+    }
+  }
+  const uint32_t in_tot = wave_inclusive_sum(s_tot);
+  const uint32_t in_act = wave_inclusive_sum(s_act);
+  const uint32_t w_max = wave_max(s_max);
+  if (lane == kWave - 1) {
+    part[wave] = in_tot;
+    part[kIdxWaves + wave] = in_act;
+    part[2 * kIdxWaves + wave] = w_max;
+  }
+  __syncthreads();
+  uint32_t p_tot = in_tot - s_tot, p_act = in_act - s_act;
+  uint32_t all_tot = 0, all_act = 0, all_max = 0;
+  for (int w = 0; w < kIdxWaves; ++w) {
+    if (w < wave) {
+      p_tot += part[w];
+      p_act += part[kIdxWaves + w];
+    }
+    all_tot += part[w];
+    all_act += part[kIdxWaves + w];
+    all_max = max(all_max, part[2 * kIdxWaves + w]);
+  }
+  for (int q = 0; q < ipt; ++q) {
+    const int b = b0 + q;
+    if (b < nb) {
+      const uint32_t v = tot[b];
+      base[b] = p_tot;
+      if (b < int(n_experts) && v > 0) {
+        expert_ids[p_act] = b;
+        esi[p_act] = p_tot;
+        ++p_act;
+      }
+      p_tot += v;
+    }
+  }
+  const uint32_t n_routed = all_tot - tot[n_experts];
+  for (uint32_t j = all_act + tid; j < n_experts; j += kIdxThreads) expert_ids[j] = -1;
+  for (uint32_t j = all_act + tid; j <= n_experts; j += kIdxThreads) esi[j] = n_routed;
+  if (tid == 0) {
+    stats[0] = all_max;
+    stats[1] = all_act;
+  }
+}
+
+// Number of slots of bucket b in chunks [0, c): walk back over earlier chunks'
+// words, kLookbackWindow at a time, adding per-chunk counts until a chunk
+// that already published its inclusive prefix.  Every earlier chunk is held
+// by a workgroup that took its ticket first and publishes its own count
+// without waiting, so the wait ends; kSpinLimit is a backstop that records
+// an error instead of spinning forever.
+__device__ uint32_t lookback(const uint64_t* flags, int64_t c, int nb, int b, uint32_t* err) {
+  uint32_t excl = 0;
+  int64_t cc = c - 1;
+  uint32_t spins = 0;
+  while (true) {
+    uint64_t f[kLookbackWindow];
+#pragma unroll
+    for (int w = 0; w < kLookbackWindow; ++w)
+      f[w] = (cc - w >= 0) ? agent_load_u64(&flags[(cc - w) * nb + b]) : kFlagPrefix;
+    int used = 0;
+    bool done = false;
+#pragma unroll
+    for (int w = 0; w < kLookbackWindow; ++w) {
+      if (done || used < w) continue;
+      const uint64_t st = f[w] & kFlagStatusMask;
+      if (st == 0) continue;  // not yet published: poll again from here
+      excl += uint32_t(f[w]);
+      used = w + 1;
+      if (st == kFlagPrefix) done = true;
+    }
+    if (done) return excl;
+    cc -= used;
+    if (used == 0 && ++spins > kSpinLimit) {
+      atomicOr(err, 1u);
+      return excl;
+    }
+  }
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void k_index_zero(IndexWorkspace ws, int64_t n_flags) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n_flags) ws.flags[i] = 0;
+  if (i == 0) {
+    *ws.ticket = 0;
+    *ws.err = 0;
+  }
+}
+
+// n_chunks == 1: one workgroup does histogram, scan and scatter.
+// n_chunks > 1: histogram + lookback + (last ticket) CSR outputs.
+__global__ __launch_bounds__(kIdxThreads) void k_index_hist(
+    const int32_t* __restrict__ ids, int64_t n_slots, uint32_t n_experts, int nbits,
+    int64_t n_chunks, IndexWorkspace ws, uint32_t* __restrict__ esi,
+    int32_t* __restrict__ expert_ids, uint32_t* __restrict__ stats, uint32_t* __restrict__ teo,
+    uint32_t* __restrict__ restore) {
+  extern __shared__ uint32_t lds[];
+  __shared__ int64_t s_chunk;
+  const int nb = int(n_experts) + 1;
+  const int tid = threadIdx.x;
+  uint32_t* hist = lds;
+
+  int64_t c = 0;
+  if (n_chunks > 1) {
+    if (tid == 0) s_chunk = int64_t(atomicAdd(ws.ticket, 1u));
+    __syncthreads();
+    c = s_chunk;
+  }
+  for (int b = tid; b < nb; b += kIdxThreads) hist[b] = 0;
+  __syncthreads();
+  chunk_histogram(ids, n_slots, c * kIdxChunk, n_experts, nbits, hist);
+  __syncthreads();
+
+  if (n_chunks > 1) {
+    for (int b = tid; b < nb; b += kIdxThreads) {
+      const uint32_t local = hist[b];
+      uint64_t* word = &ws.flags[c * nb + b];
+      uint32_t excl = 0;
+      if (c == 0) {
+        agent_store_u64(word, kFlagPrefix | local);
+      } else {
+        agent_store_u64(word, kFlagAggregate | local);
+        excl = lookback(ws.flags, c, nb, b, ws.err);
+        agent_store_u64(word, kFlagPrefix | (excl + local));
+      }
+      ws.prefix[c * nb + b] = excl;
+      hist[b] = excl + local;
+    }
+    __syncthreads();
+  }
+
+  if (c == n_chunks - 1) {
+    uint32_t* base = n_chunks > 1 ? ws.base : lds + nb;
+    finalize_counts(hist, n_experts, base, esi, expert_ids, stats);
+    if (n_chunks == 1) {
+      __syncthreads();
+      chunk_scatter(ids, n_slots, 0, n_experts, nbits, lds + nb, lds + 2 * nb, teo, restore);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kIdxThreads) void k_index_scatter(
+    const int32_t* __restrict__ ids, int64_t n_slots, uint32_t n_experts, int nbits,
+    IndexWorkspace ws, uint32_t* __restrict__ teo, uint32_t* __restrict__ restore) {
+  extern __shared__ uint32_t lds[];
+  const int nb = int(n_experts) + 1;
+  const int64_t c = blockIdx.x;
+  uint32_t* off = lds;
+  for (int b = threadIdx.x; b < nb; b += kIdxThreads) off[b] = ws.base[b] + ws.prefix[c * nb + b];
+  __syncthreads();
+  chunk_scatter(ids, n_slots, c * kIdxChunk, n_experts, nbits, off, lds + nb, teo, restore);
+}
+
+int64_t index_chunks(int64_t n_slots) {
+  return n_slots <= kIdxChunk ? 1 : (n_slots + kIdxChunk - 1) / kIdxChunk;
+}
+
+size_t index_workspace_bytes(int64_t n_slots, int n_experts) {
+  const size_t c = size_t(index_chunks(n_slots)), nb = size_t(n_experts) + 1;
+  return 256 + align256(c * nb * 8) + align256(c * nb * 4) + align256(nb * 4);
+}
+
+IndexWorkspace index_workspace_carve(void* ws, int64_t n_slots, int n_experts) {
+  const size_t c = size_t(index_chunks(n_slots)), nb = size_t(n_experts) + 1;
+  char* p = static_cast<char*>(ws);
+  IndexWorkspace w;
+  w.err = reinterpret_cast<uint32_t*>(p);
+  w.ticket = reinterpret_cast<uint32_t*>(p + 4);
+  p += 256;
+  w.flags = reinterpret_cast<uint64_t*>(p);
+  p += align256(c * nb * 8);
+  w.prefix = reinterpret_cast<uint32_t*>(p);
+  p += align256(c * nb * 4);
+  w.base = reinterpret_cast<uint32_t*>(p);
+  return w;
+}
+
+hipError_t launch_create_indices(const int32_t* ids, int64_t n_slots, int n_experts,
+                                 uint32_t* teo, uint32_t* esi, uint32_t* restore,
+                                 int32_t* expert_ids, uint32_t* stats, void* wsp, hipStream_t s) {
+  const int64_t chunks = index_chunks(n_slots);
+  const int nb = n_experts + 1;
+  const int nbits = 32 - __builtin_clz(uint32_t(n_experts));
+  const IndexWorkspace ws = index_workspace_carve(wsp, n_slots, n_experts);
+  if (chunks == 1) {
+    const size_t lds = size_t(2 + kIdxWaves) * nb * sizeof(uint32_t);
+    hipLaunchKernelGGL(k_index_hist, dim3(1), dim3(kIdxThreads), lds, s, ids, n_slots,
+                       uint32_t(n_experts), nbits, chunks, ws, esi, expert_ids, stats, teo, restore);
+    return hipGetLastError();
+  }
+  const int64_t n_flags = chunks * nb;
+  hipLaunchKernelGGL(k_index_zero, dim3(uint32_t((n_flags + 255) / 256)), dim3(256), 0, s, ws,
+                     n_flags);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_index_hist, dim3(uint32_t(chunks)), dim3(kIdxThreads),
+                     size_t(nb) * sizeof(uint32_t), s, ids, n_slots, uint32_t(n_experts), nbits,
+                     chunks, ws, esi, expert_ids, stats, teo, restore);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_index_scatter, dim3(uint32_t(chunks)), dim3(kIdxThreads),
+                     size_t(1 + kIdxWaves) * nb * sizeof(uint32_t), s, ids, n_slots,
+                     uint32_t(n_experts), nbits, ws, teo, restore);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,50 @@
+// Host-side launchers of the routing kernels.  Arguments are validated by the
+// C entry points before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- index stage geometry -------------------------------------------------
+// One workgroup of kIdxThreads threads owns a chunk of kIdxChunk consecutive
+// slots; each of its waves owns kIdxRounds*64 consecutive slots of the chunk.
+constexpr int kIdxThreads = 512;
+constexpr int kIdxWaves = kIdxThreads / 64;
+constexpr int kIdxRounds = 8;
+constexpr int64_t kIdxChunk = int64_t(kIdxThreads) * kIdxRounds;
+
+struct IndexWorkspace {
+  uint32_t* err;        // [1]  nonzero if a cross-workgroup wait gave up
+  uint32_t* ticket;     // [1]  chunk ticket counter
+  uint64_t* flags;      // [chunks][E+1] (status << 32 | count) lookback words
+  uint32_t* prefix;     // [chunks][E+1] slots of bucket b in chunks before c
+  uint32_t* base;       // [E+1]         first position of bucket b
+};
+
+int64_t index_chunks(int64_t n_slots);
+size_t index_workspace_bytes(int64_t n_slots, int n_experts);
+IndexWorkspace index_workspace_carve(void* ws, int64_t n_slots, int n_experts);
+
+hipError_t launch_mask_padding(int32_t* ids, int64_t n_rows, int top_k, const int32_t* count,
+                               int tp_rank, hipStream_t s);
+
+hipError_t launch_create_indices(const int32_t* ids, int64_t n_slots, int n_experts,
+                                 uint32_t* teo, uint32_t* esi, uint32_t* restore,
+                                 int32_t* expert_ids, uint32_t* stats, void* ws, hipStream_t s);
+
+hipError_t launch_dispatch_bf16(const uint16_t* x, int64_t n_rows, int hidden, int top_k,
+                                const uint32_t* restore, uint16_t* out, int64_t out_rows,
+                                hipStream_t s);
+
+hipError_t launch_dispatch_mxfp4(const uint16_t* x, int64_t n_rows, int hidden, int top_k,
+                                 const uint32_t* restore, uint8_t* q, uint8_t* scales,
+                                 int64_t out_rows, hipStream_t s);
+
+hipError_t launch_combine(const uint16_t* y, int64_t y_rows, const float* w,
+                          const uint32_t* restore, int64_t n_rows, int hidden, int top_k,
+                          uint16_t* out, hipStream_t s);
+
+}  // namespace moe

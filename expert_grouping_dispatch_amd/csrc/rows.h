@@ -1,0 +1,57 @@
+// Per-token helpers of the row kernels (dispatch and combine).
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+constexpr int kRowThreads = 256;
+constexpr int kMaxTopK = 1024;
+
+// Row kernels loop over tokens when there are more than kMaxRowBlocks.
+constexpr int64_t kMaxRowBlocks = int64_t(1) << 20;
+inline uint32_t row_grid(int64_t n_rows) {
+  return uint32_t(n_rows < kMaxRowBlocks ? n_rows : kMaxRowBlocks);
+}
+
+// Positions >= limit are skipped; limit <= 0xFFFFFFFF so the sentinel is
+// always skipped.
+inline uint32_t position_limit(int64_t rows) {
+  return rows >= int64_t(0xFFFFFFFFu) ? 0xFFFFFFFFu : uint32_t(rows);
+}
+
+// Wave 0 collects, in ascending j, the positions restore[t*top_k + j] that
+// are routed and below `limit` (and their weights, when w is given) into LDS.
+// Returns the count to the whole workgroup.
+__device__ __forceinline__ int gather_routed(const uint32_t* __restrict__ restore,
+                                             const float* __restrict__ w, int64_t t, int top_k,
+                                             uint32_t limit, uint32_t* s_pos, float* s_w,
+                                             int* s_n) {
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const uint64_t below = lanes_below();
+    int n = 0;
+    for (int j0 = 0; j0 < top_k; j0 += kWave) {
+      const int j = j0 + lane;
+      uint32_t p = kSent;
+      float wt = 0.0f;
+      if (j < top_k) {
+        p = restore[t * top_k + j];
+        if (w != nullptr) wt = w[t * top_k + j];
+      }
+      const bool ok = p < limit;
+      const uint64_t m = __ballot(ok);
+      if (ok) {
+        const int r = n + __popcll(m & below);
+        s_pos[r] = p;
+        if (s_w != nullptr) s_w[r] = wt;
+      }
+      n += __popcll(m);
+    }
+    if (lane == 0) *s_n = n;
+  }
+  __syncthreads();
+  return *s_n;
+}
+
+}  // namespace moe

@@ -1,0 +1,91 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+The library must export every function include/moe_route.h declares, and
+argument errors must be rejected on the host before any device call.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_route.h")
+
+mod = pytest.importorskip("expert_grouping_dispatch_amd")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_path():
+    assert declared_functions() == sorted([
+        "moe_error_string", "moe_mask_padding", "moe_create_indices_workspace_bytes",
+        "moe_create_indices", "moe_dispatch", "moe_dispatch_mxfp4", "moe_combine"])
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", mod.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(mod.lib, name) is not None
+
+
+def test_error_strings():
+    assert mod.moe_error_string(0) == "ok"
+    for s in range(1, 5):
+        assert mod.moe_error_string(s) not in ("ok", "unknown status")
+    assert mod.moe_error_string(99) == "unknown status"
+
+
+def test_workspace_size_query():
+    f = mod.moe_create_indices_workspace_bytes
+    assert f(-1, 8) == 0 and f(10, 0) == 0 and f(10, 1025) == 0 and f(2 ** 32 - 1, 8) == 0
+    prev = 0
+    for s in (0, 1, 4096, 4097, 100000, 524288, 2 ** 32 - 2):
+        b = f(s, 256)
+        assert b >= prev and b % 256 == 0
+        prev = b
+    assert f(524288, 1024) > f(524288, 8)
+
+
+P = ctypes.c_void_p
+
+
+def test_invalid_arguments_rejected_on_host():
+    L = mod.lib
+    fake = P(256)  # never dereferenced: every call below fails its argument check first
+    cnt = P(512)
+    assert L.moe_mask_padding(None, 4, 2, cnt, 0, None) == 1          # null map
+    assert L.moe_mask_padding(fake, 4, 0, cnt, 0, None) == 1          # top_k < 1
+    assert L.moe_mask_padding(fake, 4, 2, None, 0, None) == 1         # null count
+    assert L.moe_mask_padding(fake, 4, 2, cnt, -1, None) == 1         # tp_rank < 0
+    assert L.moe_mask_padding(fake, -1, 2, cnt, 0, None) == 1         # n_rows < 0
+    assert L.moe_mask_padding(fake, 2 ** 31, 2, cnt, 0, None) == 1    # slots reach the sentinel
+    ws = mod.moe_create_indices_workspace_bytes(100, 8)
+    args = [fake, 100, 8, fake, fake, fake, fake, fake, fake, ws, None]
+    bad = list(args); bad[2] = 0
+    assert L.moe_create_indices(*bad) == 1                          # n_experts < 1
+    bad = list(args); bad[2] = 1025
+    assert L.moe_create_indices(*bad) == 1                          # n_experts too large
+    bad = list(args); bad[8] = None
+    assert L.moe_create_indices(*bad) == 1                          # null workspace
+    bad = list(args); bad[8] = P(256 + 8)
+    assert L.moe_create_indices(*bad) == 1                          # misaligned workspace
+    bad = list(args); bad[9] = ws - 1
+    assert L.moe_create_indices(*bad) == 2                          # workspace too small
+    assert L.moe_dispatch(fake, 10, 12, 2, fake, fake, 20, None) == 1        # hidden % 8
+    assert L.moe_dispatch(P(258), 10, 16, 2, fake, fake, 20, None) == 1      # misaligned x
+    assert L.moe_dispatch(fake, 10, 16, 0, fake, fake, 20, None) == 1        # top_k < 1
+    assert L.moe_dispatch(fake, 10, 16, 1025, fake, fake, 20, None) == 1     # top_k too large
+    assert L.moe_dispatch_mxfp4(fake, 10, 48, 2, fake, fake, fake, 20, 0, None) == 1  # hidden % 32
+    assert L.moe_dispatch_mxfp4(fake, 10, 64, 2, fake, fake, fake, 20, 1, None) == 1  # flags
+    assert L.moe_combine(fake, 20, fake, fake, 10, 12, 2, fake, None) == 1   # hidden % 8
+    assert L.moe_combine(fake, 20, None, fake, 10, 16, 2, fake, None) == 1   # null weights
+    assert L.moe_combine(fake, -1, fake, fake, 10, 16, 2, fake, None) == 1   # y_rows < 0

@@ -1,0 +1,331 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bit-exact on the masked routing map, every index output, bf16 dispatch rows
+and MXFP4 payload / scale bytes; combine within 1 bf16 ulp (and bit-exact
+in practice: the kernel does the same fp32 operations in the same order).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_common import (SENT, bf16_from_bits, bf16_ulp_distance, check_indices, gpu_available, i32,
+                              run_path, u16, u32)
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+mod = pytest.importorskip("expert_grouping_dispatch_amd") if gpu_available() else None
+DEV = "cuda"
+
+
+def _oracle_front(ids, real, n_experts, tp_rank=0):
+    m = oracle.mask_routing_padding(ids, real, tp_rank)
+    return m, oracle.create_indices(m, n_experts)
+
+
+def _check_combine(got_bits, want_bits, exact=True):
+    d = bf16_ulp_distance(got_bits, want_bits)
+    assert int(d.max(initial=0)) <= 1, f"combine off by {int(d.max())} ulp"
+    if exact:
+        assert int((got_bits != want_bits).sum()) == 0, "combine not bit-exact"
+
+
+def _full_check(ids, w, real, n_experts, x, y, variants, tp_rank=0):
+    """Everything compared element by element."""
+    n, k = ids.shape
+    res = run_path(mod, ids, real, n_experts, x, y, w, variants, tp_rank)
+    m, ref = _oracle_front(ids, real, n_experts, tp_rank)
+    np.testing.assert_array_equal(i32(res["ids"]), m)
+    check_indices(res, ref)
+    v = ref["n_routed"]
+    xb = u16(x)
+    if "bf16" in variants:
+        want = oracle.dispatch(xb, ref["token_expert_order"], k, v)
+        np.testing.assert_array_equal(u16(res["dispatch"][:v]), want)
+    if "mxfp4" in variants:
+        wq, ws = oracle.dispatch_mxfp4(xb, ref["token_expert_order"], k, v)
+        np.testing.assert_array_equal(res["q"][:v].cpu().numpy(), wq)
+        np.testing.assert_array_equal(res["scales"][:v].cpu().numpy(), ws)
+    if y is not None:
+        want = oracle.combine(u16(y), w, ref["restore_token_order"], k)
+        _check_combine(u16(res["combine"]), want)
+    return res, ref
+
+
+# ---------------------------------------------------------------- workloads
+@pytest.mark.parametrize("cfg", [0, 1, 3])
+def test_workload_full(cfg):
+    w = workloads.WORKLOADS[cfg]
+    ids, wts, real = workloads.make_routing(w, cfg)
+    x, y = workloads.make_dense(w, cfg, DEV)
+    print(f"[parity] workload {w.name} full", flush=True)
+    _full_check(ids, wts, real, w.n_experts, x, y, ("bf16", "mxfp4"))
+
+
+def _sample_positions(esi, a, v, g, n=512):
+    edges = np.concatenate([esi[:a], np.maximum(esi[1:a + 1].astype(np.int64) - 1, 0)]).astype(np.int64)
+    rnd = g.integers(0, v, size=n)
+    return np.unique(np.concatenate([edges, rnd, [0, v - 1]]))
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_workload_full_size_sampled(cfg):
+    """Full-size workloads in the launch configuration the bench times:
+    indices compared in full, dispatch / MXFP4 / combine on sampled rows."""
+    w = workloads.WORKLOADS[cfg]
+    ids, wts, real = workloads.make_routing(w, cfg)
+    x, y = workloads.make_dense(w, cfg, DEV)
+    print(f"[parity] workload {w.name} full size, sampled rows", flush=True)
+    res = run_path(mod, ids, real, w.n_experts, x, y, wts, ("bf16", "mxfp4"))
+    m, ref = _oracle_front(ids, real, w.n_experts)
+    np.testing.assert_array_equal(i32(res["ids"]), m)
+    check_indices(res, ref)
+    k, v = w.top_k, ref["n_routed"]
+    g = np.random.default_rng(cfg)
+    pos = _sample_positions(ref["expert_start_indices"], int(ref["expert_usage_stats"][1]), v, g)
+    src = ref["token_expert_order"][pos].astype(np.int64) // k
+    xs = u16(x[torch.from_numpy(src).to(DEV)])
+    pidx = torch.from_numpy(pos).to(DEV)
+    np.testing.assert_array_equal(u16(res["dispatch"][pidx]), xs)
+    wq, wsc = oracle.mxfp4_quantize(xs)
+    np.testing.assert_array_equal(res["q"][pidx].cpu().numpy(), wq)
+    np.testing.assert_array_equal(res["scales"][pidx].cpu().numpy(), wsc)
+    # combine on sampled tokens (including masked rows when there are any)
+    toks = np.unique(np.concatenate([g.integers(0, w.n_rows, size=256), [0, w.n_rows - 1, real - 1,
+                                                                          min(real, w.n_rows - 1)]]))
+    rs = ref["restore_token_order"].reshape(w.n_rows, k)[toks]
+    used = np.unique(rs[rs != SENT]).astype(np.int64)
+    ysub = u16(y[torch.from_numpy(used).to(DEV)])
+    remap = np.full(rs.shape, SENT, np.uint32)
+    remap[rs != SENT] = np.searchsorted(used, rs[rs != SENT].astype(np.int64))
+    want = oracle.combine(ysub, wts[toks], remap.reshape(-1), k)
+    got = u16(res["combine"][torch.from_numpy(toks).to(DEV)])
+    _check_combine(got, want)
+    # property at full size: rows with nothing routed are +0
+    if real < w.n_rows:
+        assert int(res["combine"][real:].view(torch.int16).abs().max()) == 0
+
+
+# ---------------------------------------------------------------- edge cases
+def _rand_case(seed, n, k, e, h, kind="uniform", real=None):
+    g = np.random.default_rng(seed)
+    if kind == "uniform":
+        ids = g.integers(0, e, size=(n, k))
+    elif kind == "distinct":
+        ids = np.argsort(g.random((n, e)), axis=1)[:, :k]
+    elif kind == "garbage":
+        pool = np.array([-1, -9, e, e + 5, 2 ** 31 - 1, -2 ** 31] + list(range(e)))
+        ids = g.choice(pool, size=(n, k))
+    elif kind == "one_expert":
+        ids = np.full((n, k), e // 2)
+    elif kind == "half_empty":  # only even experts used -> zero-token experts in between
+        ids = 2 * g.integers(0, max(1, e // 2), size=(n, k))
+    else:
+        raise ValueError(kind)
+    w = g.random((n, k)).astype(np.float32)
+    x = bf16_from_bits(oracle.f32_to_bf16_rne(g.standard_normal((n, h)).astype(np.float32)), DEV)
+    y = bf16_from_bits(oracle.f32_to_bf16_rne(g.standard_normal((n * k, h)).astype(np.float32)), DEV)
+    return ids.astype(np.int32), w, (n if real is None else real), x, y
+
+
+@pytest.mark.parametrize("real_case", ["zero", "one", "n_minus_1", "n", "n_plus_5", "neg3"])
+@pytest.mark.parametrize("tp_rank", [0, 1])
+def test_real_count_edges(real_case, tp_rank):
+    n, k, e, h = 300, 4, 16, 64
+    real = {"zero": 0, "one": 1, "n_minus_1": n - 1, "n": n, "n_plus_5": n + 5, "neg3": -3}[real_case]
+    real += tp_rank * n
+    ids, w, _, x, y = _rand_case(1, n, k, e, h, "garbage")
+    _full_check(ids, w, real, e, x, y, ("bf16", "mxfp4"), tp_rank)
+
+
+CASES = {
+    # name: (seed, n, k, e, h, kind)
+    "k1": (2, 500, 1, 8, 32, "uniform"),
+    "k_equals_e": (3, 200, 8, 8, 64, "distinct"),
+    "duplicates": (4, 333, 6, 5, 32, "uniform"),
+    "garbage_ids": (5, 257, 3, 7, 96, "garbage"),
+    "one_expert": (6, 1500, 4, 64, 32, "one_expert"),
+    "zero_token_experts": (7, 2000, 4, 256, 64, "half_empty"),
+    "e1": (8, 100, 2, 1, 32, "uniform"),
+    "e1024": (9, 3000, 8, 1024, 32, "distinct"),
+    "k64": (10, 90, 64, 128, 32, "distinct"),
+    "k100": (11, 40, 100, 300, 32, "distinct"),
+    "ragged_chunks": (12, 3 * 4096 // 4 + 77, 4, 32, 32, "uniform"),
+    "many_chunks_skewed": (13, 40000, 8, 256, 32, "one_expert"),
+    "many_chunks": (14, 70000, 8, 256, 32, "distinct"),
+    "h8_bf16_only": (15, 64, 2, 4, 8, "uniform"),
+    "h_large": (16, 20, 2, 4, 16384, "uniform"),
+    "h_ragged_vectors": (17, 30, 3, 6, 32 * 37, "uniform"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_edge_case(name):
+    seed, n, k, e, h, kind = CASES[name]
+    ids, w, real, x, y = _rand_case(seed, n, k, e, h, kind)
+    variants = ("bf16",) if h % 32 else ("bf16", "mxfp4")
+    print(f"[parity] edge {name}: n={n} k={k} e={e} h={h}", flush=True)
+    _full_check(ids, w, real, e, x, y, variants)
+
+
+def test_empty_input():
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    y = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    ids = np.zeros((0, 4), np.int32)
+    res = run_path(mod, ids, 0, 16, x, y, np.zeros((0, 4), np.float32))
+    assert u32(res["expert_start_indices"]).tolist() == [0] * 17
+    assert i32(res["expert_ids"]).tolist() == [-1] * 16
+    assert u32(res["expert_usage_stats"]).tolist() == [0, 0]
+
+
+def test_mxfp4_special_blocks():
+    """Zero / negative-zero / subnormal / largest-finite / tie blocks, bit-exact."""
+    g = np.random.default_rng(21)
+    h = 32 * 64
+    rows = []
+    allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = allb[((allb >> 7) & 0xFF) != 0xFF]
+    rows.append(np.zeros(h, np.uint16))
+    rows.append(np.full(h, 0x8000, np.uint16))
+    rows.append(g.integers(0, 0x80, size=h).astype(np.uint16))                # subnormals
+    rows.append((g.integers(0, 0x80, size=h) | 0x8000).astype(np.uint16))
+    rows.append(np.full(h, 0x7F7F, np.uint16))                                 # max finite
+    rows.append(g.choice(finite, size=h).astype(np.uint16))                    # every exponent
+    ties = oracle.f32_to_bf16_rne(np.array([4.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0, 6.0, 1.0, 0.5,
+                                            -0.25, -2.5, -5.0, 0.0] * 2, np.float32))
+    rows.append(np.tile(ties, h // 32))
+    for s in range(6):  # mixed-magnitude blocks with one large outlier each
+        f = g.standard_normal(h).astype(np.float32)
+        f[::32] *= 10.0 ** (s * 6 - 15)
+        rows.append(oracle.f32_to_bf16_rne(f))
+    xb = np.stack(rows)
+    n = xb.shape[0]
+    x = bf16_from_bits(xb, DEV)
+    ids = np.stack([np.arange(3) + t for t in range(n)]).astype(np.int32) % 5
+    res = run_path(mod, ids, n, 5, x, None, np.ones((n, 3), np.float32), ("mxfp4",))
+    ref = oracle.create_indices(ids, 5)
+    wq, ws = oracle.dispatch_mxfp4(xb, ref["token_expert_order"], 3, ref["n_routed"])
+    np.testing.assert_array_equal(res["scales"].cpu().numpy(), ws)
+    np.testing.assert_array_equal(res["q"].cpu().numpy(), wq)
+
+
+def test_combine_no_fma_and_fixed_order():
+    """Two cancelling products that a fused multiply-add would leave as 2^-30,
+    and +1, +2^-30, -1 that only the fixed j order sums to +0."""
+    h = 8
+    w = np.array([[-(1 + 2.0 ** -23), 1 + 2.0 ** -23, 0.0], [1.0, 1.0, 1.0]], np.float32)
+    yv = np.zeros((6, h), np.float32)
+    yv[0] = yv[1] = 1 + 2.0 ** -7
+    yv[3], yv[4], yv[5] = 1.0, 2.0 ** -30, -1.0
+    y = bf16_from_bits(oracle.f32_to_bf16_rne(yv), DEV)
+    restore = torch.from_numpy(np.array([0, 1, SENT, 3, 4, 5], np.uint32).view(np.int32)).to(DEV).view(torch.uint32)
+    out = torch.empty((2, h), dtype=torch.bfloat16, device=DEV)
+    mod.moe_combine(y, torch.from_numpy(w).to(DEV), restore, 3, out)
+    got = u16(out)
+    want = oracle.combine(u16(y), w, u32(restore), 3)
+    assert np.all(want == 0)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_positions_outside_buffer_are_skipped():
+    n, k, e, h = 50, 2, 4, 32
+    ids, w, real, x, y = _rand_case(30, n, k, e, h)
+    ref = oracle.create_indices(ids, e)
+    restore = torch.from_numpy(ref["restore_token_order"].view(np.int32)).to(DEV).view(torch.uint32)
+    limit = 37
+    out = torch.zeros((limit, h), dtype=torch.bfloat16, device=DEV)
+    mod.moe_dispatch(x, k, restore, out)
+    want = oracle.dispatch(u16(x), ref["token_expert_order"], k, ref["n_routed"])[:limit]
+    np.testing.assert_array_equal(u16(out), want)
+    comb = torch.empty((n, h), dtype=torch.bfloat16, device=DEV)
+    mod.moe_combine(y[:limit], torch.from_numpy(w).to(DEV), restore, k, comb)
+    r2 = ref["restore_token_order"].copy()
+    r2[(r2 != SENT) & (r2 >= limit)] = SENT
+    _check_combine(u16(comb), oracle.combine(u16(y[:limit]), w, r2, k))
+
+
+def test_deterministic_under_skew():
+    w = workloads.WORKLOADS[2]
+    ids, wts, real = workloads.make_routing(w, 2)
+    w_small = workloads.scaled(w, hidden=64)
+    x, y = workloads.make_dense(w_small, 2, DEV)
+    a = run_path(mod, ids, real, w.n_experts, x, y, wts)
+    b = run_path(mod, ids, real, w.n_experts, x, y, wts)
+    for key in ("token_expert_order", "restore_token_order", "expert_start_indices"):
+        assert torch.equal(a[key].view(torch.int32), b[key].view(torch.int32))
+    assert torch.equal(a["combine"].view(torch.int16), b["combine"].view(torch.int16))
+    assert torch.equal(a["q"], b["q"])
+
+
+def test_lookback_error_word_clear():
+    ids, w, real, x, y = _rand_case(40, 30000, 8, 256, 32, "distinct")
+    res = run_path(mod, ids, real, 256, x, y, w, ("bf16",))
+    assert int(res["workspace"][:4].view(torch.int32).item()) == 0
+
+
+def test_argument_errors_on_device():
+    idx = mod.alloc_indices(100, 8, DEV)
+    ids = torch.zeros(100, dtype=torch.int32, device=DEV)
+    small = idx["workspace"][:16]
+    with pytest.raises(mod.MoeError) as e:
+        mod.moe_create_indices(ids, 8, idx["token_expert_order"], idx["expert_start_indices"],
+                               idx["restore_token_order"], idx["expert_ids"], idx["expert_usage_stats"], small)
+    assert e.value.status == 2
+    x = torch.zeros((10, 32), dtype=torch.bfloat16, device=DEV)
+    q, s = mod.alloc_dispatch_mxfp4(100, 32, DEV)
+    with pytest.raises(mod.MoeError) as e:
+        mod.moe_dispatch_mxfp4(x, 10, idx["restore_token_order"], q, s, flags=1)
+    assert e.value.status == 1
+
+
+def test_graph_replay_with_device_count():
+    """Capture mask+indices+dispatch+combine once; change only the device-side
+    count between replays (with eager work in between) and check each replay."""
+    n, k, e, h = 2048, 4, 64, 64
+    ids0, w, _, x, y = _rand_case(50, n, k, e, h, "distinct")
+    d_ids = torch.from_numpy(ids0).to(DEV)
+    d_src = d_ids.clone()
+    cnt = torch.tensor([n], dtype=torch.int32, device=DEV)
+    d_w = torch.from_numpy(w).to(DEV)
+    idx = mod.alloc_indices(n * k, e, DEV)
+    disp = mod.alloc_dispatch(n * k, h, DEV)
+    q, sc = mod.alloc_dispatch_mxfp4(n * k, h, DEV)
+    comb = torch.empty((n, h), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        mod.moe_mask_padding(d_ids, cnt, 0)
+        mod.moe_create_indices(d_ids, e, idx["token_expert_order"], idx["expert_start_indices"],
+                               idx["restore_token_order"], idx["expert_ids"], idx["expert_usage_stats"],
+                               idx["workspace"])
+        mod.moe_dispatch(x, k, idx["restore_token_order"], disp)
+        mod.moe_dispatch_mxfp4(x, k, idx["restore_token_order"], q, sc)
+        mod.moe_combine(y, d_w, idx["restore_token_order"], k, comb)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+        d_ids.copy_(d_src)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for real in (1500, 7, 2048, 0, 1999):
+        d_ids.copy_(d_src)  # the mask works in place; restore the unmasked map eagerly
+        cnt.fill_(real)
+        torch.cuda.synchronize()
+        _ = (x.float() * 2).sum()  # unrelated eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        m, ref = _oracle_front(ids0, real, e)
+        np.testing.assert_array_equal(i32(d_ids), m)
+        res = dict(idx)
+        check_indices(res, ref)
+        v = ref["n_routed"]
+        np.testing.assert_array_equal(u16(disp[:v]), oracle.dispatch(u16(x), ref["token_expert_order"], k, v))
+        wq, wsc = oracle.dispatch_mxfp4(u16(x), ref["token_expert_order"], k, v)
+        np.testing.assert_array_equal(q[:v].cpu().numpy(), wq)
+        np.testing.assert_array_equal(sc[:v].cpu().numpy(), wsc)
+        _check_combine(u16(comb), oracle.combine(u16(y), w, ref["restore_token_order"], k))
