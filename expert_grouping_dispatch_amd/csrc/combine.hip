@@ -16,6 +16,32 @@ namespace moe {
 namespace {
 
 constexpr int kBatch = 8;
+#ifndef MOE_COMBINE_UNROLL
+#define MOE_COMBINE_UNROLL 1
+#endif
+#ifndef MOE_COMBINE_NT_STORE
+#define MOE_COMBINE_NT_STORE 1
+#endif
+#ifndef MOE_COMBINE_NT_LOAD
+#define MOE_COMBINE_NT_LOAD 1
+#endif
+constexpr int kCombineMaxThreads = 1024;
+constexpr int kCombineUnroll = MOE_COMBINE_UNROLL;
+
+// One workgroup covers a whole row: each lane owns kCombineUnroll vectors of
+// 8 hidden elements, spread evenly over at most kCombineMaxThreads lanes.
+int combine_threads(int h16) {
+  const int per_lane = kCombineUnroll * ((h16 + kCombineUnroll * kCombineMaxThreads - 1) /
+                                         (kCombineUnroll * kCombineMaxThreads));
+  int t = (h16 + per_lane - 1) / per_lane;
+  t = (t + 63) / 64 * 64;
+  return t < 64 ? 64 : (t > kCombineMaxThreads ? kCombineMaxThreads : t);
+}
+
+__device__ __forceinline__ u32x4 load_y(const u32x4* p) {
+  if constexpr (MOE_COMBINE_NT_LOAD) return __builtin_nontemporal_load(p);
+  else return *p;
+}
 
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -35,47 +61,108 @@ __device__ __forceinline__ void accumulate(float (&acc)[8], const u32x4& v, floa
 
 }  // namespace
 
-__global__ __launch_bounds__(kRowThreads) void k_combine(
+// K > 0: top_k == K, positions and weights in scalar registers; K == 0: any
+// top_k, compacted into LDS by wave 0 and consumed kBatch rows at a time.
+template <int K>
+__global__ __launch_bounds__(kCombineMaxThreads) void k_combine(
     const u32x4* __restrict__ y, const float* __restrict__ w, const uint32_t* __restrict__ restore,
     int64_t n_rows, int h16, int top_k, u32x4* __restrict__ out, uint32_t limit) {
-  __shared__ uint32_t s_pos[kMaxTopK];
-  __shared__ float s_w[kMaxTopK];
+  __shared__ uint32_t s_pos[K > 0 ? 1 : kMaxTopK];
+  __shared__ float s_w[K > 0 ? 1 : kMaxTopK];
   __shared__ int s_n;
+  constexpr int KR = K > 0 ? K : 1;
+  constexpr int kRows = K > 0 ? K : kBatch;  // rows loaded at once
+  const int nthreads = blockDim.x;
   for (int64_t t = blockIdx.x; t < n_rows; t += gridDim.x) {
-  const int n = gather_routed(restore, w, t, top_k, limit, s_pos, s_w, &s_n);
-  u32x4* dst = out + t * h16;
-  for (int c = threadIdx.x; c < h16; c += kRowThreads) {
-    float acc[8];
+    uint32_t pos[KR];
+    float wt[KR];
+    int n = 0;
+    if constexpr (K > 0)
+      uniform_slots<K, true>(restore, w, t, limit, pos, wt);
+    else
+      n = gather_routed(restore, w, t, top_k, limit, s_pos, s_w, &s_n);
+    u32x4* dst = out + t * h16;
+    for (int c0 = threadIdx.x; c0 < h16; c0 += nthreads * kCombineUnroll) {
+      float acc[kCombineUnroll][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-    for (int j0 = 0; j0 < n; j0 += kBatch) {
-      u32x4 v[kBatch];
+      for (int u = 0; u < kCombineUnroll; ++u)
 #pragma unroll
-      for (int jj = 0; jj < kBatch; ++jj)
-        if (j0 + jj < n) v[jj] = __builtin_nontemporal_load(y + int64_t(s_pos[j0 + jj]) * h16 + c);
+        for (int e = 0; e < 8; ++e) acc[u][e] = 0.0f;
+      const int nrows = K > 0 ? K : n;
+      for (int j0 = 0; j0 < nrows; j0 += kRows) {
+        u32x4 v[kCombineUnroll][kRows];
 #pragma unroll
-      for (int jj = 0; jj < kBatch; ++jj)
-        if (j0 + jj < n) accumulate(acc, v[jj], s_w[j0 + jj]);
+        for (int jj = 0; jj < kRows; ++jj) {
+          const uint32_t p = K > 0 ? pos[jj] : (j0 + jj < n ? s_pos[j0 + jj] : kSent);
+          if (p != kSent) {
+            const u32x4* row = y + int64_t(p) * h16;
+#pragma unroll
+            for (int u = 0; u < kCombineUnroll; ++u) {
+              const int c = c0 + u * nthreads;
+              if (c < h16) v[u][jj] = load_y(row + c);
+            }
+          }
+        }
+#pragma unroll
+        for (int jj = 0; jj < kRows; ++jj) {
+          const uint32_t p = K > 0 ? pos[jj] : (j0 + jj < n ? s_pos[j0 + jj] : kSent);
+          if (p != kSent) {
+            const float wj = K > 0 ? wt[jj] : s_w[j0 + jj];
+#pragma unroll
+            for (int u = 0; u < kCombineUnroll; ++u)
+              if (c0 + u * nthreads < h16) accumulate(acc[u], v[u][jj], wj);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kCombineUnroll; ++u) {
+        const int c = c0 + u * nthreads;
+        if (c < h16) {
+          u32x4 o;
+          o.x = bf16_rne(acc[u][0]) | (bf16_rne(acc[u][1]) << 16);
+          o.y = bf16_rne(acc[u][2]) | (bf16_rne(acc[u][3]) << 16);
+          o.z = bf16_rne(acc[u][4]) | (bf16_rne(acc[u][5]) << 16);
+          o.w = bf16_rne(acc[u][6]) | (bf16_rne(acc[u][7]) << 16);
+          if constexpr (MOE_COMBINE_NT_STORE) __builtin_nontemporal_store(o, dst + c);
+          else dst[c] = o;
+        }
+      }
     }
-    u32x4 o;
-    o.x = bf16_rne(acc[0]) | (bf16_rne(acc[1]) << 16);
-    o.y = bf16_rne(acc[2]) | (bf16_rne(acc[3]) << 16);
-    o.z = bf16_rne(acc[4]) | (bf16_rne(acc[5]) << 16);
-    o.w = bf16_rne(acc[6]) | (bf16_rne(acc[7]) << 16);
-    __builtin_nontemporal_store(o, dst + c);
-  }
-  __syncthreads();  // s_pos / s_w are rewritten for the next token
+    if constexpr (K == 0) __syncthreads();  // s_pos / s_w are rewritten for the next token
   }
 }
+
+namespace {
+
+template <int K>
+hipError_t launch_k(const u32x4* y, const float* w, const uint32_t* restore, int64_t n_rows,
+                    int h16, int top_k, u32x4* out, uint32_t limit, hipStream_t s) {
+  hipLaunchKernelGGL(k_combine<K>, dim3(row_grid(n_rows)), dim3(combine_threads(h16)), 0, s, y, w,
+                     restore, n_rows, h16, top_k, out, limit);
+  return hipGetLastError();
+}
+
+}  // namespace
 
 hipError_t launch_combine(const uint16_t* y, int64_t y_rows, const float* w,
                           const uint32_t* restore, int64_t n_rows, int hidden, int top_k,
                           uint16_t* out, hipStream_t s) {
   if (n_rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_combine, dim3(row_grid(n_rows)), dim3(kRowThreads), 0, s,
-                     reinterpret_cast<const u32x4*>(y), w, restore, n_rows, hidden / 8, top_k,
-                     reinterpret_cast<u32x4*>(out), position_limit(y_rows));
-  return hipGetLastError();
+  const u32x4* yv = reinterpret_cast<const u32x4*>(y);
+  u32x4* ov = reinterpret_cast<u32x4*>(out);
+  const int h16 = hidden / 8;
+  const uint32_t lim = position_limit(y_rows);
+  switch (top_k) {
+    case 1: return launch_k<1>(yv, w, restore, n_rows, h16, top_k, ov, lim, s);
+    case 2: return launch_k<2>(yv, w, restore, n_rows, h16, top_k, ov, lim, s);
+    case 3: return launch_k<3>(yv, w, restore, n_rows, h16, top_k, ov, lim, s);
+    case 4: return launch_k<4>(yv, w, restore, n_rows, h16, top_k, ov, lim, s);
+    case 5: return launch_k<5>(yv, w, restore, n_rows, h16, top_k, ov, lim, s);
+    case 6: return launch_k<6>(yv, w, restore, n_rows, h16, top_k, ov, lim, s);
+    case 7: return launch_k<7>(yv, w, restore, n_rows, h16, top_k, ov, lim, s);
+    case 8: return launch_k<8>(yv, w, restore, n_rows, h16, top_k, ov, lim, s);
+    default: return launch_k<0>(yv, w, restore, n_rows, h16, top_k, ov, lim, s);
+  }
 }
 
 }  // namespace moe

@@ -12,7 +12,44 @@ namespace moe {
 
 namespace {
 
-constexpr int kLoadsInFlight = 4;  // 16-byte vectors each lane loads before storing
+#ifndef MOE_DISPATCH_LOADS
+#define MOE_DISPATCH_LOADS 4
+#endif
+#ifndef MOE_DISPATCH_THREADS
+#define MOE_DISPATCH_THREADS 256
+#endif
+#ifndef MOE_MXFP4_THREADS
+#define MOE_MXFP4_THREADS 256
+#endif
+// Cache policy (measured on MI355X: plain loads and stores for the bf16 row
+// fan-out, plain loads and non-temporal stores for the MXFP4 rows).
+#ifndef MOE_DISPATCH_NT_LOAD
+#define MOE_DISPATCH_NT_LOAD 0
+#endif
+#ifndef MOE_DISPATCH_NT_STORE
+#define MOE_DISPATCH_NT_STORE 0
+#endif
+#ifndef MOE_MXFP4_NT_LOAD
+#define MOE_MXFP4_NT_LOAD 0
+#endif
+#ifndef MOE_MXFP4_NT_STORE
+#define MOE_MXFP4_NT_STORE 1
+#endif
+constexpr int kLoadsInFlight = MOE_DISPATCH_LOADS;  // 16-byte vectors each lane loads before storing
+constexpr int kDispatchThreads = MOE_DISPATCH_THREADS;
+constexpr int kMxThreads = MOE_MXFP4_THREADS;
+
+template <bool kNonTemporal>
+__device__ __forceinline__ u32x4 load_vec(const u32x4* p) {
+  if constexpr (kNonTemporal) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <bool kNonTemporal>
+__device__ __forceinline__ void store_vec(u32x4* p, const u32x4& v) {
+  if constexpr (kNonTemporal) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
 
 // E8M0 exponent of a 32-element block from the largest magnitude, given as
 // the 15-bit magnitude of a bf16 pattern: floor(log2 amax) - 2, clamped to
@@ -51,100 +88,172 @@ __device__ __forceinline__ uint32_t e2m1_nibble(uint32_t bits, float mul) {
 
 }  // namespace
 
-__global__ __launch_bounds__(kRowThreads) void k_dispatch_bf16(
-    const u32x4* __restrict__ x, int64_t n_rows, int h16, int top_k, const uint32_t* __restrict__ restore,
-    u32x4* __restrict__ out, uint32_t limit) {
-  __shared__ uint32_t s_pos[kMaxTopK];
+// K > 0: top_k == K and the positions sit in scalar registers; K == 0: any
+// top_k, positions compacted into LDS by wave 0.
+template <int K>
+__global__ __launch_bounds__(kDispatchThreads) void k_dispatch_bf16(
+    const u32x4* __restrict__ x, int64_t n_rows, int h16, int top_k,
+    const uint32_t* __restrict__ restore, u32x4* __restrict__ out, uint32_t limit) {
+  __shared__ uint32_t s_pos[K > 0 ? 1 : kMaxTopK];
   __shared__ int s_n;
+  constexpr int KR = K > 0 ? K : 1;
   for (int64_t t = blockIdx.x; t < n_rows; t += gridDim.x) {
-  const int n = gather_routed(restore, nullptr, t, top_k, limit, s_pos, nullptr, &s_n);
-  const u32x4* src = x + t * h16;
-  for (int c0 = threadIdx.x; n > 0 && c0 < h16; c0 += kRowThreads * kLoadsInFlight) {
-    u32x4 v[kLoadsInFlight];
+    uint32_t pos[KR];
+    float unused[KR];
+    int n;
+    if constexpr (K > 0) {
+      uniform_slots<K, false>(restore, nullptr, t, limit, pos, unused);
+      n = 0;
 #pragma unroll
-    for (int u = 0; u < kLoadsInFlight; ++u) {
-      const int c = c0 + u * kRowThreads;
-      if (c < h16) v[u] = __builtin_nontemporal_load(src + c);
+      for (int j = 0; j < K; ++j) n += pos[j] != kSent ? 1 : 0;
+    } else {
+      n = gather_routed(restore, nullptr, t, top_k, limit, s_pos, nullptr, &s_n);
     }
-    for (int j = 0; j < n; ++j) {
-      u32x4* dst = out + int64_t(s_pos[j]) * h16;
+    const u32x4* src = x + t * h16;
+    for (int c0 = threadIdx.x; n > 0 && c0 < h16; c0 += kDispatchThreads * kLoadsInFlight) {
+      u32x4 v[kLoadsInFlight];
 #pragma unroll
       for (int u = 0; u < kLoadsInFlight; ++u) {
-        const int c = c0 + u * kRowThreads;
-        if (c < h16) __builtin_nontemporal_store(v[u], dst + c);
+        const int c = c0 + u * kDispatchThreads;
+        if (c < h16) v[u] = load_vec<MOE_DISPATCH_NT_LOAD>(src + c);
+      }
+      const int nj = K > 0 ? K : n;
+#pragma unroll
+      for (int j = 0; j < nj; ++j) {
+        const uint32_t p = K > 0 ? pos[j] : s_pos[j];
+        if (p == kSent) continue;
+        u32x4* dst = out + int64_t(p) * h16;
+#pragma unroll
+        for (int u = 0; u < kLoadsInFlight; ++u) {
+          const int c = c0 + u * kDispatchThreads;
+          if (c < h16) store_vec<MOE_DISPATCH_NT_STORE>(dst + c, v[u]);
+        }
       }
     }
-  }
-  __syncthreads();  // s_pos is rewritten for the next token
+    if constexpr (K == 0) __syncthreads();  // s_pos is rewritten for the next token
   }
 }
 
 // One lane per 32-element block: 4 x 16-byte loads, 16 bytes of payload and
 // one scale byte per routed position.
-__global__ __launch_bounds__(kRowThreads) void k_dispatch_mxfp4(
-    const u32x4* __restrict__ x, int64_t n_rows, int h16, int top_k, const uint32_t* __restrict__ restore,
-    u32x4* __restrict__ q, uint8_t* __restrict__ scales, uint32_t limit) {
-  __shared__ uint32_t s_pos[kMaxTopK];
+template <int K>
+__global__ __launch_bounds__(kMxThreads) void k_dispatch_mxfp4(
+    const u32x4* __restrict__ x, int64_t n_rows, int h16, int top_k,
+    const uint32_t* __restrict__ restore, u32x4* __restrict__ q, uint8_t* __restrict__ scales,
+    uint32_t limit) {
+  __shared__ uint32_t s_pos[K > 0 ? 1 : kMaxTopK];
   __shared__ int s_n;
+  constexpr int KR = K > 0 ? K : 1;
   const int nblk = h16 / 4;
   for (int64_t t = blockIdx.x; t < n_rows; t += gridDim.x) {
-  const int n = gather_routed(restore, nullptr, t, top_k, limit, s_pos, nullptr, &s_n);
-  const u32x4* src = x + t * h16;
-  for (int b = threadIdx.x; n > 0 && b < nblk; b += kRowThreads) {
-    uint32_t w[16];
+    uint32_t pos[KR];
+    float unused[KR];
+    int n;
+    if constexpr (K > 0) {
+      uniform_slots<K, false>(restore, nullptr, t, limit, pos, unused);
+      n = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const u32x4 v = __builtin_nontemporal_load(src + 4 * b + u);
-      w[4 * u + 0] = v.x;
-      w[4 * u + 1] = v.y;
-      w[4 * u + 2] = v.z;
-      w[4 * u + 3] = v.w;
+      for (int j = 0; j < K; ++j) n += pos[j] != kSent ? 1 : 0;
+    } else {
+      n = gather_routed(restore, nullptr, t, top_k, limit, s_pos, nullptr, &s_n);
     }
-    uint32_t amax = 0;
+    const u32x4* src = x + t * h16;
+    for (int b = threadIdx.x; n > 0 && b < nblk; b += kMxThreads) {
+      uint32_t w[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) amax = max(amax, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
-    const int se = mx_scale_exponent(amax);
-    const float mul = __uint_as_float(uint32_t(127 - se) << 23);
-    uint32_t packed[4] = {0u, 0u, 0u, 0u};
+      for (int u = 0; u < 4; ++u) {
+        const u32x4 v = load_vec<MOE_MXFP4_NT_LOAD>(src + 4 * b + u);
+        w[4 * u + 0] = v.x;
+        w[4 * u + 1] = v.y;
+        w[4 * u + 2] = v.z;
+        w[4 * u + 3] = v.w;
+      }
+      uint32_t amax = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t byte = e2m1_nibble(w[i] & 0xFFFFu, mul) | (e2m1_nibble(w[i] >> 16, mul) << 4);
-      packed[i / 4] |= byte << (8 * (i % 4));
+      for (int i = 0; i < 16; ++i) amax = max(amax, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+      const int se = mx_scale_exponent(amax);
+      const float mul = __uint_as_float(uint32_t(127 - se) << 23);
+      uint32_t packed[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t byte =
+            e2m1_nibble(w[i] & 0xFFFFu, mul) | (e2m1_nibble(w[i] >> 16, mul) << 4);
+        packed[i / 4] |= byte << (8 * (i % 4));
+      }
+      u32x4 pv;
+      pv.x = packed[0];
+      pv.y = packed[1];
+      pv.z = packed[2];
+      pv.w = packed[3];
+      const uint8_t sbyte = uint8_t(se + 127);
+      const int nj = K > 0 ? K : n;
+#pragma unroll
+      for (int j = 0; j < nj; ++j) {
+        const uint32_t p32 = K > 0 ? pos[j] : s_pos[j];
+        if (p32 == kSent) continue;
+        const int64_t p = p32;
+        store_vec<MOE_MXFP4_NT_STORE>(q + p * nblk + b, pv);
+        scales[p * nblk + b] = sbyte;
+      }
     }
-    u32x4 pv;
-    pv.x = packed[0];
-    pv.y = packed[1];
-    pv.z = packed[2];
-    pv.w = packed[3];
-    const uint8_t sbyte = uint8_t(se + 127);
-    for (int j = 0; j < n; ++j) {
-      const int64_t p = s_pos[j];
-      __builtin_nontemporal_store(pv, q + p * nblk + b);
-      scales[p * nblk + b] = sbyte;
-    }
-  }
-  __syncthreads();  // s_pos is rewritten for the next token
+    if constexpr (K == 0) __syncthreads();  // s_pos is rewritten for the next token
   }
 }
+
+namespace {
+
+template <template <int> class Launch, typename... Args>
+hipError_t by_top_k(int top_k, Args... args) {
+  switch (top_k) {
+    case 1: return Launch<1>::run(args...);
+    case 2: return Launch<2>::run(args...);
+    case 3: return Launch<3>::run(args...);
+    case 4: return Launch<4>::run(args...);
+    case 5: return Launch<5>::run(args...);
+    case 6: return Launch<6>::run(args...);
+    case 7: return Launch<7>::run(args...);
+    case 8: return Launch<8>::run(args...);
+    default: return Launch<0>::run(args...);
+  }
+}
+
+template <int K>
+struct LaunchBf16 {
+  static hipError_t run(const u32x4* x, int64_t n_rows, int h16, int top_k, const uint32_t* restore,
+                        u32x4* out, uint32_t limit, hipStream_t s) {
+    hipLaunchKernelGGL(k_dispatch_bf16<K>, dim3(row_grid(n_rows)), dim3(kDispatchThreads), 0, s, x,
+                       n_rows, h16, top_k, restore, out, limit);
+    return hipGetLastError();
+  }
+};
+
+template <int K>
+struct LaunchMxfp4 {
+  static hipError_t run(const u32x4* x, int64_t n_rows, int h16, int top_k, const uint32_t* restore,
+                        u32x4* q, uint8_t* scales, uint32_t limit, hipStream_t s) {
+    hipLaunchKernelGGL(k_dispatch_mxfp4<K>, dim3(row_grid(n_rows)), dim3(kMxThreads), 0, s, x,
+                       n_rows, h16, top_k, restore, q, scales, limit);
+    return hipGetLastError();
+  }
+};
+
+}  // namespace
 
 hipError_t launch_dispatch_bf16(const uint16_t* x, int64_t n_rows, int hidden, int top_k,
                                 const uint32_t* restore, uint16_t* out, int64_t out_rows,
                                 hipStream_t s) {
   if (n_rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_dispatch_bf16, dim3(row_grid(n_rows)), dim3(kRowThreads), 0, s,
-                     reinterpret_cast<const u32x4*>(x), n_rows, hidden / 8, top_k, restore,
-                     reinterpret_cast<u32x4*>(out), position_limit(out_rows));
-  return hipGetLastError();
+  return by_top_k<LaunchBf16>(top_k, reinterpret_cast<const u32x4*>(x), n_rows, hidden / 8, top_k,
+                              restore, reinterpret_cast<u32x4*>(out), position_limit(out_rows), s);
 }
 
 hipError_t launch_dispatch_mxfp4(const uint16_t* x, int64_t n_rows, int hidden, int top_k,
                                  const uint32_t* restore, uint8_t* q, uint8_t* scales,
                                  int64_t out_rows, hipStream_t s) {
   if (n_rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_dispatch_mxfp4, dim3(row_grid(n_rows)), dim3(kRowThreads), 0, s,
-                     reinterpret_cast<const u32x4*>(x), n_rows, hidden / 8, top_k, restore,
-                     reinterpret_cast<u32x4*>(q), scales, position_limit(out_rows));
-  return hipGetLastError();
+  return by_top_k<LaunchMxfp4>(top_k, reinterpret_cast<const u32x4*>(x), n_rows, hidden / 8, top_k,
+                               restore, reinterpret_cast<u32x4*>(q), scales,
+                               position_limit(out_rows), s);
 }
 
 }  // namespace moe

@@ -5,8 +5,10 @@
 
 namespace moe {
 
-constexpr int kRowThreads = 256;
 constexpr int kMaxTopK = 1024;
+// top_k up to this value is handled with per-wave uniform slot registers;
+// larger top_k goes through an LDS list built by wave 0.
+constexpr int kMaxUniformTopK = 8;
 
 // Row kernels loop over tokens when there are more than kMaxRowBlocks.
 constexpr int64_t kMaxRowBlocks = int64_t(1) << 20;
@@ -18,6 +20,27 @@ inline uint32_t row_grid(int64_t n_rows) {
 // always skipped.
 inline uint32_t position_limit(int64_t rows) {
   return rows >= int64_t(0xFFFFFFFFu) ? 0xFFFFFFFFu : uint32_t(rows);
+}
+
+// Positions restore[t*K + j] (and weights) for a compile-time K: the
+// addresses are uniform across the workgroup, so every wave holds them in
+// scalar registers and no LDS or barrier is needed.  Positions >= limit
+// become kSent.
+template <int K, bool kWeights>
+__device__ __forceinline__ void uniform_slots(const uint32_t* __restrict__ restore,
+                                              const float* __restrict__ w, int64_t t,
+                                              uint32_t limit, uint32_t (&pos)[K], float (&wt)[K]) {
+  const uint32_t* r = restore + t * K;
+  uint32_t raw[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) raw[j] = r[j];
+  if constexpr (kWeights) {
+    const float* wr = w + t * K;
+#pragma unroll
+    for (int j = 0; j < K; ++j) wt[j] = wr[j];
+  }
+#pragma unroll
+  for (int j = 0; j < K; ++j) pos[j] = raw[j] < limit ? raw[j] : kSent;
 }
 
 // Wave 0 collects, in ascending j, the positions restore[t*top_k + j] that
