@@ -133,6 +133,8 @@ def main():
     ap.add_argument("--workload", default="large_prefill_stress", choices=sorted(workloads.BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 1 GiB device copy before the steps (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -174,6 +176,14 @@ def main():
             lambda: moe.moe_dispatch_mxfp4(x, k, idx["restore_token_order"], q, sc),
             lambda: moe.moe_combine(y, d_w, idx["restore_token_order"], k, comb),
         ]
+
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        log("calibration copy of 1073741824 bytes done")
 
     calls = stage_calls()
     for _ in range(args.warmup):
