@@ -25,7 +25,10 @@ constexpr uint64_t kFlagAggregate = uint64_t(1) << 32;  // count of this chunk o
 constexpr uint64_t kFlagPrefix = uint64_t(2) << 32;     // count of chunks [0, c]
 constexpr uint64_t kFlagStatusMask = ~uint64_t(0xFFFFFFFFu);
 constexpr uint32_t kSpinLimit = 1u << 20;
-constexpr int kLookbackWindow = 8;
+#ifndef MOE_LOOKBACK_WINDOW
+#define MOE_LOOKBACK_WINDOW 8
+#endif
+constexpr int kLookbackWindow = MOE_LOOKBACK_WINDOW;
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 

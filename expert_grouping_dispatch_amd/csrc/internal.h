@@ -11,9 +11,15 @@ namespace moe {
 // ---- index stage geometry -------------------------------------------------
 // One workgroup of kIdxThreads threads owns a chunk of kIdxChunk consecutive
 // slots; each of its waves owns kIdxRounds*64 consecutive slots of the chunk.
-constexpr int kIdxThreads = 512;
+#ifndef MOE_IDX_THREADS
+#define MOE_IDX_THREADS 512
+#endif
+#ifndef MOE_IDX_ROUNDS
+#define MOE_IDX_ROUNDS 8
+#endif
+constexpr int kIdxThreads = MOE_IDX_THREADS;
 constexpr int kIdxWaves = kIdxThreads / 64;
-constexpr int kIdxRounds = 8;
+constexpr int kIdxRounds = MOE_IDX_ROUNDS;
 constexpr int64_t kIdxChunk = int64_t(kIdxThreads) * kIdxRounds;
 
 struct IndexWorkspace {
