@@ -38,6 +38,74 @@ bool slots_ok(int64_t n_rows, int32_t top_k) {
   return n_rows <= int64_t(0xFFFFFFFEu) / top_k;  // every slot index and position < sentinel
 }
 
+template <typename IdT>
+int mask_padding(IdT* routing_map, int64_t n_rows, int32_t top_k, const int32_t* real_token_count,
+                 int32_t tp_rank, void* stream) {
+  if (!slots_ok(n_rows, top_k) || tp_rank < 0 || real_token_count == nullptr ||
+      !aligned(real_token_count, 4))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (n_rows > 0 && (routing_map == nullptr || !aligned(routing_map, sizeof(IdT))))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (const int d = check_device()) return d;
+  return launched(moe::launch_mask_padding(routing_map, n_rows, top_k, real_token_count, tp_rank,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+template <typename IdT>
+int create_indices(const IdT* topk_ids, int64_t n_slots, int32_t n_experts,
+                   uint32_t* token_expert_order, uint32_t* expert_start_indices,
+                   uint32_t* restore_token_order, int32_t* expert_ids,
+                   uint32_t* expert_usage_stats, uint32_t* scales_offset, uint32_t scales_align,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_slots < 0 || n_slots > int64_t(0xFFFFFFFEu) || n_experts < 1 || n_experts > MOE_MAX_EXPERTS)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (expert_start_indices == nullptr || expert_ids == nullptr || expert_usage_stats == nullptr ||
+      workspace == nullptr)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (n_slots > 0 && (topk_ids == nullptr || token_expert_order == nullptr ||
+                      restore_token_order == nullptr))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (scales_offset != nullptr &&
+      (scales_align < 1 || uint64_t(n_slots) + uint64_t(n_experts) * scales_align >= 0xFFFFFFFFull))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(topk_ids, sizeof(IdT)) || !aligned(token_expert_order, 4) ||
+      !aligned(expert_start_indices, 4) || !aligned(restore_token_order, 4) ||
+      !aligned(expert_ids, 4) || !aligned(expert_usage_stats, 4) || !aligned(scales_offset, 4) ||
+      !aligned(workspace, 256))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < moe::index_workspace_bytes(n_slots, n_experts))
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (const int d = check_device()) return d;
+  return launched(moe::launch_create_indices(topk_ids, n_slots, n_experts, token_expert_order,
+                                             expert_start_indices, restore_token_order, expert_ids,
+                                             expert_usage_stats, scales_offset, scales_align,
+                                             workspace, static_cast<hipStream_t>(stream)));
+}
+
+int combine(const uint16_t* y, int64_t y_rows, const float* router_weights,
+            const uint32_t* restore_token_order, int64_t n_rows, int32_t hidden, int32_t top_k,
+            bool epilogue, float scale, const uint16_t* residual, uint16_t* output_tokens,
+            void* stream) {
+  if (!slots_ok(n_rows, top_k) || hidden <= 0 || hidden % 8 != 0 || y_rows < 0)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (n_rows > 0 && (router_weights == nullptr || restore_token_order == nullptr ||
+                     output_tokens == nullptr))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (y_rows > 0 && y == nullptr) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(y, 16) || !aligned(output_tokens, 16) || !aligned(router_weights, 4) ||
+      !aligned(restore_token_order, 4) || !aligned(residual, 16))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (residual != nullptr && n_rows > 0) {  // the residual rows must not overlap the output
+    const uintptr_t bytes = uintptr_t(n_rows) * uintptr_t(hidden) * 2;
+    const uintptr_t r = reinterpret_cast<uintptr_t>(residual), o = reinterpret_cast<uintptr_t>(output_tokens);
+    if (r < o + bytes && o < r + bytes) return MOE_ERR_INVALID_ARGUMENT;
+  }
+  if (const int d = check_device()) return d;
+  return launched(moe::launch_combine(y, y_rows, router_weights, restore_token_order, n_rows,
+                                      hidden, top_k, epilogue, scale, residual, output_tokens,
+                                      static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -55,14 +123,12 @@ const char* moe_error_string(int status) {
 
 int moe_mask_padding(int32_t* routing_map, int64_t n_rows, int32_t top_k,
                      const int32_t* real_token_count, int32_t tp_rank, void* stream) {
-  if (!slots_ok(n_rows, top_k) || tp_rank < 0 || real_token_count == nullptr ||
-      !aligned(real_token_count, 4))
-    return MOE_ERR_INVALID_ARGUMENT;
-  if (n_rows > 0 && (routing_map == nullptr || !aligned(routing_map, 4)))
-    return MOE_ERR_INVALID_ARGUMENT;
-  if (const int d = check_device()) return d;
-  return launched(moe::launch_mask_padding(routing_map, n_rows, top_k, real_token_count, tp_rank,
-                                           static_cast<hipStream_t>(stream)));
+  return mask_padding(routing_map, n_rows, top_k, real_token_count, tp_rank, stream);
+}
+
+int moe_mask_padding_i64(int64_t* routing_map, int64_t n_rows, int32_t top_k,
+                         const int32_t* real_token_count, int32_t tp_rank, void* stream) {
+  return mask_padding(routing_map, n_rows, top_k, real_token_count, tp_rank, stream);
 }
 
 size_t moe_create_indices_workspace_bytes(int64_t n_slots, int32_t n_experts) {
@@ -74,27 +140,23 @@ size_t moe_create_indices_workspace_bytes(int64_t n_slots, int32_t n_experts) {
 int moe_create_indices(const int32_t* topk_ids, int64_t n_slots, int32_t n_experts,
                        uint32_t* token_expert_order, uint32_t* expert_start_indices,
                        uint32_t* restore_token_order, int32_t* expert_ids,
-                       uint32_t* expert_usage_stats, void* workspace, size_t workspace_bytes,
+                       uint32_t* expert_usage_stats, uint32_t* scales_offset,
+                       uint32_t scales_align, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  if (n_slots < 0 || n_slots > int64_t(0xFFFFFFFEu) || n_experts < 1 || n_experts > MOE_MAX_EXPERTS)
-    return MOE_ERR_INVALID_ARGUMENT;
-  if (expert_start_indices == nullptr || expert_ids == nullptr || expert_usage_stats == nullptr ||
-      workspace == nullptr)
-    return MOE_ERR_INVALID_ARGUMENT;
-  if (n_slots > 0 && (topk_ids == nullptr || token_expert_order == nullptr ||
-                      restore_token_order == nullptr))
-    return MOE_ERR_INVALID_ARGUMENT;
-  if (!aligned(topk_ids, 4) || !aligned(token_expert_order, 4) || !aligned(expert_start_indices, 4) ||
-      !aligned(restore_token_order, 4) || !aligned(expert_ids, 4) ||
-      !aligned(expert_usage_stats, 4) || !aligned(workspace, 256))
-    return MOE_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < moe::index_workspace_bytes(n_slots, n_experts))
-    return MOE_ERR_WORKSPACE_TOO_SMALL;
-  if (const int d = check_device()) return d;
-  return launched(moe::launch_create_indices(topk_ids, n_slots, n_experts, token_expert_order,
-                                             expert_start_indices, restore_token_order, expert_ids,
-                                             expert_usage_stats, workspace,
-                                             static_cast<hipStream_t>(stream)));
+  return create_indices(topk_ids, n_slots, n_experts, token_expert_order, expert_start_indices,
+                        restore_token_order, expert_ids, expert_usage_stats, scales_offset,
+                        scales_align, workspace, workspace_bytes, stream);
+}
+
+int moe_create_indices_i64(const int64_t* topk_ids, int64_t n_slots, int32_t n_experts,
+                           uint32_t* token_expert_order, uint32_t* expert_start_indices,
+                           uint32_t* restore_token_order, int32_t* expert_ids,
+                           uint32_t* expert_usage_stats, uint32_t* scales_offset,
+                           uint32_t scales_align, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return create_indices(topk_ids, n_slots, n_experts, token_expert_order, expert_start_indices,
+                        restore_token_order, expert_ids, expert_usage_stats, scales_offset,
+                        scales_align, workspace, workspace_bytes, stream);
 }
 
 int moe_dispatch(const uint16_t* input_tokens, int64_t n_rows, int32_t hidden, int32_t top_k,
@@ -116,36 +178,37 @@ int moe_dispatch(const uint16_t* input_tokens, int64_t n_rows, int32_t hidden, i
 int moe_dispatch_mxfp4(const uint16_t* input_tokens, int64_t n_rows, int32_t hidden,
                        int32_t top_k, const uint32_t* restore_token_order, uint8_t* out_q,
                        uint8_t* out_scales, int64_t out_rows, uint32_t flags, void* stream) {
+  const bool packed = (flags & MOE_MXFP4_PACKED_ROWS) != 0;
   if (!slots_ok(n_rows, top_k) || hidden <= 0 || hidden % MOE_MXFP4_BLOCK != 0 || out_rows < 0 ||
-      flags != 0)
+      (flags & ~(MOE_MXFP4_EVEN_SCALE | MOE_MXFP4_PACKED_ROWS)) != 0)
     return MOE_ERR_INVALID_ARGUMENT;
+  if (packed && (hidden % 512 != 0 || out_scales != nullptr)) return MOE_ERR_INVALID_ARGUMENT;
   if (n_rows > 0 && (input_tokens == nullptr || restore_token_order == nullptr))
     return MOE_ERR_INVALID_ARGUMENT;
-  if (out_rows > 0 && (out_q == nullptr || out_scales == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  if (out_rows > 0 && (out_q == nullptr || (!packed && out_scales == nullptr)))
+    return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(input_tokens, 16) || !aligned(out_q, 16) || !aligned(restore_token_order, 4))
     return MOE_ERR_INVALID_ARGUMENT;
   if (const int d = check_device()) return d;
   return launched(moe::launch_dispatch_mxfp4(input_tokens, n_rows, hidden, top_k,
                                              restore_token_order, out_q, out_scales, out_rows,
+                                             (flags & MOE_MXFP4_EVEN_SCALE) != 0, packed,
                                              static_cast<hipStream_t>(stream)));
 }
 
 int moe_combine(const uint16_t* y, int64_t y_rows, const float* router_weights,
                 const uint32_t* restore_token_order, int64_t n_rows, int32_t hidden,
                 int32_t top_k, uint16_t* output_tokens, void* stream) {
-  if (!slots_ok(n_rows, top_k) || hidden <= 0 || hidden % 8 != 0 || y_rows < 0)
-    return MOE_ERR_INVALID_ARGUMENT;
-  if (n_rows > 0 && (router_weights == nullptr || restore_token_order == nullptr ||
-                     output_tokens == nullptr))
-    return MOE_ERR_INVALID_ARGUMENT;
-  if (y_rows > 0 && y == nullptr) return MOE_ERR_INVALID_ARGUMENT;
-  if (!aligned(y, 16) || !aligned(output_tokens, 16) || !aligned(router_weights, 4) ||
-      !aligned(restore_token_order, 4))
-    return MOE_ERR_INVALID_ARGUMENT;
-  if (const int d = check_device()) return d;
-  return launched(moe::launch_combine(y, y_rows, router_weights, restore_token_order, n_rows,
-                                      hidden, top_k, output_tokens,
-                                      static_cast<hipStream_t>(stream)));
+  return combine(y, y_rows, router_weights, restore_token_order, n_rows, hidden, top_k, false,
+                 1.0f, nullptr, output_tokens, stream);
+}
+
+int moe_combine_epilogue(const uint16_t* y, int64_t y_rows, const float* router_weights,
+                         const uint32_t* restore_token_order, int64_t n_rows, int32_t hidden,
+                         int32_t top_k, float scale, const uint16_t* residual,
+                         uint16_t* output_tokens, void* stream) {
+  return combine(y, y_rows, router_weights, restore_token_order, n_rows, hidden, top_k, true,
+                 scale, residual, output_tokens, stream);
 }
 
 }  // extern "C"

@@ -59,14 +59,33 @@ __device__ __forceinline__ void accumulate(float (&acc)[8], const u32x4& v, floa
   }
 }
 
+// fl(scale * acc), then fl(... + residual) when a residual row is given.
+__device__ __forceinline__ void epilogue(float (&acc)[8], float scale,
+                                         const u32x4* __restrict__ residual, int64_t idx) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = __fmul_rn(scale, acc[e]);
+  if (residual != nullptr) {
+    const u32x4 r = residual[idx];
+    const uint32_t word[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] = __fadd_rn(acc[2 * e], __uint_as_float(word[e] << 16));
+      acc[2 * e + 1] = __fadd_rn(acc[2 * e + 1], __uint_as_float(word[e] & 0xFFFF0000u));
+    }
+  }
+}
+
 }  // namespace
 
 // K > 0: top_k == K, positions and weights in scalar registers; K == 0: any
 // top_k, compacted into LDS by wave 0 and consumed kBatch rows at a time.
-template <int K>
+// kEpilogue: out = bf16(fl(fl(scale*acc) + residual)), residual may be null
+// (it never overlaps out).
+template <int K, bool kEpilogue>
 __global__ __launch_bounds__(kCombineMaxThreads) void k_combine(
     const u32x4* __restrict__ y, const float* __restrict__ w, const uint32_t* __restrict__ restore,
-    int64_t n_rows, int h16, int top_k, u32x4* __restrict__ out, uint32_t limit) {
+    int64_t n_rows, int h16, int top_k, float scale, const u32x4* __restrict__ residual,
+    u32x4* __restrict__ out, uint32_t limit) {
   __shared__ uint32_t s_pos[K > 0 ? 1 : kMaxTopK];
   __shared__ float s_w[K > 0 ? 1 : kMaxTopK];
   __shared__ int s_n;
@@ -118,6 +137,7 @@ __global__ __launch_bounds__(kCombineMaxThreads) void k_combine(
       for (int u = 0; u < kCombineUnroll; ++u) {
         const int c = c0 + u * nthreads;
         if (c < h16) {
+          if constexpr (kEpilogue) epilogue(acc[u], scale, residual, t * h16 + c);
           u32x4 o;
           o.x = bf16_rne(acc[u][0]) | (bf16_rne(acc[u][1]) << 16);
           o.y = bf16_rne(acc[u][2]) | (bf16_rne(acc[u][3]) << 16);
@@ -136,9 +156,14 @@ namespace {
 
 template <int K>
 hipError_t launch_k(const u32x4* y, const float* w, const uint32_t* restore, int64_t n_rows,
-                    int h16, int top_k, u32x4* out, uint32_t limit, hipStream_t s) {
-  hipLaunchKernelGGL(k_combine<K>, dim3(row_grid(n_rows)), dim3(combine_threads(h16)), 0, s, y, w,
-                     restore, n_rows, h16, top_k, out, limit);
+                    int h16, int top_k, bool epi, float scale, const u32x4* residual, u32x4* out,
+                    uint32_t limit, hipStream_t s) {
+  if (epi)
+    hipLaunchKernelGGL((k_combine<K, true>), dim3(row_grid(n_rows)), dim3(combine_threads(h16)), 0,
+                       s, y, w, restore, n_rows, h16, top_k, scale, residual, out, limit);
+  else
+    hipLaunchKernelGGL((k_combine<K, false>), dim3(row_grid(n_rows)), dim3(combine_threads(h16)),
+                       0, s, y, w, restore, n_rows, h16, top_k, scale, residual, out, limit);
   return hipGetLastError();
 }
 
@@ -146,23 +171,28 @@ hipError_t launch_k(const u32x4* y, const float* w, const uint32_t* restore, int
 
 hipError_t launch_combine(const uint16_t* y, int64_t y_rows, const float* w,
                           const uint32_t* restore, int64_t n_rows, int hidden, int top_k,
-                          uint16_t* out, hipStream_t s) {
+                          bool epilogue, float scale, const uint16_t* residual, uint16_t* out,
+                          hipStream_t s) {
   if (n_rows == 0) return hipSuccess;
   const u32x4* yv = reinterpret_cast<const u32x4*>(y);
+  const u32x4* rv = reinterpret_cast<const u32x4*>(residual);
   u32x4* ov = reinterpret_cast<u32x4*>(out);
   const int h16 = hidden / 8;
   const uint32_t lim = position_limit(y_rows);
+#define MOE_COMBINE_CASE(KK) \
+  case KK: return launch_k<KK>(yv, w, restore, n_rows, h16, top_k, epilogue, scale, rv, ov, lim, s);
   switch (top_k) {
-    case 1: return launch_k<1>(yv, w, restore, n_rows, h16, top_k, ov, lim, s);
-    case 2: return launch_k<2>(yv, w, restore, n_rows, h16, top_k, ov, lim, s);
-    case 3: return launch_k<3>(yv, w, restore, n_rows, h16, top_k, ov, lim, s);
-    case 4: return launch_k<4>(yv, w, restore, n_rows, h16, top_k, ov, lim, s);
-    case 5: return launch_k<5>(yv, w, restore, n_rows, h16, top_k, ov, lim, s);
-    case 6: return launch_k<6>(yv, w, restore, n_rows, h16, top_k, ov, lim, s);
-    case 7: return launch_k<7>(yv, w, restore, n_rows, h16, top_k, ov, lim, s);
-    case 8: return launch_k<8>(yv, w, restore, n_rows, h16, top_k, ov, lim, s);
-    default: return launch_k<0>(yv, w, restore, n_rows, h16, top_k, ov, lim, s);
+    MOE_COMBINE_CASE(1)
+    MOE_COMBINE_CASE(2)
+    MOE_COMBINE_CASE(3)
+    MOE_COMBINE_CASE(4)
+    MOE_COMBINE_CASE(5)
+    MOE_COMBINE_CASE(6)
+    MOE_COMBINE_CASE(7)
+    MOE_COMBINE_CASE(8)
+    default: return launch_k<0>(yv, w, restore, n_rows, h16, top_k, epilogue, scale, rv, ov, lim, s);
   }
+#undef MOE_COMBINE_CASE
 }
 
 }  // namespace moe

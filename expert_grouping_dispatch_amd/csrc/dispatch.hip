@@ -53,11 +53,15 @@ __device__ __forceinline__ void store_vec(u32x4* p, const u32x4& v) {
 
 // E8M0 exponent of a 32-element block from the largest magnitude, given as
 // the 15-bit magnitude of a bf16 pattern: floor(log2 amax) - 2, clamped to
-// [-127, 127]; -127 for an all-zero block.
+// [-127, 127]; -127 for an all-zero block.  kEven rounds amax to one
+// mantissa bit (ties away) first: the floor gains 1 when the 7-bit mantissa
+// is >= 0.75 (0x60).  Subnormal amax clamps to -127 either way.
+template <bool kEven>
 __device__ __forceinline__ int mx_scale_exponent(uint32_t amax) {
   if (amax == 0) return -127;
   const int ef = int(amax >> 7);
-  const int fl = ef > 0 ? ef - 127 : -133 + (31 - __clz(amax));  // subnormal: m * 2^-133
+  int fl = ef > 0 ? ef - 127 : -133 + (31 - __clz(amax));  // subnormal: m * 2^-133
+  if (kEven && ef > 0 && (amax & 0x7Fu) >= 0x60u) fl += 1;
   const int se = fl - 2;
   return se < -127 ? -127 : se;
 }
@@ -135,11 +139,13 @@ __global__ __launch_bounds__(kDispatchThreads) void k_dispatch_bf16(
 }
 
 // One lane per 32-element block: 4 x 16-byte loads, 16 bytes of payload and
-// one scale byte per routed position.
-template <int K>
+// one scale byte per routed position.  kPacked: one row of 17*nblk bytes per
+// slot, the 16*nblk payload bytes first and the nblk scale bytes after them
+// (the launcher checks 17*nblk % 16 == 0, i.e. hidden % 512 == 0).
+template <int K, bool kEven, bool kPacked>
 __global__ __launch_bounds__(kMxThreads) void k_dispatch_mxfp4(
     const u32x4* __restrict__ x, int64_t n_rows, int h16, int top_k,
-    const uint32_t* __restrict__ restore, u32x4* __restrict__ q, uint8_t* __restrict__ scales,
+    const uint32_t* __restrict__ restore, uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
     uint32_t limit) {
   __shared__ uint32_t s_pos[K > 0 ? 1 : kMaxTopK];
   __shared__ int s_n;
@@ -171,7 +177,7 @@ __global__ __launch_bounds__(kMxThreads) void k_dispatch_mxfp4(
       uint32_t amax = 0;
 #pragma unroll
       for (int i = 0; i < 16; ++i) amax = max(amax, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
-      const int se = mx_scale_exponent(amax);
+      const int se = mx_scale_exponent<kEven>(amax);
       const float mul = __uint_as_float(uint32_t(127 - se) << 23);
       uint32_t packed[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -192,8 +198,14 @@ __global__ __launch_bounds__(kMxThreads) void k_dispatch_mxfp4(
         const uint32_t p32 = K > 0 ? pos[j] : s_pos[j];
         if (p32 == kSent) continue;
         const int64_t p = p32;
-        store_vec<MOE_MXFP4_NT_STORE>(q + p * nblk + b, pv);
-        scales[p * nblk + b] = sbyte;
+        if constexpr (kPacked) {
+          uint8_t* row = q + p * (int64_t(nblk) * 17);  // 16 payload bytes + 1 scale byte per block
+          store_vec<MOE_MXFP4_NT_STORE>(reinterpret_cast<u32x4*>(row) + b, pv);
+          row[int64_t(nblk) * 16 + b] = sbyte;
+        } else {
+          store_vec<MOE_MXFP4_NT_STORE>(reinterpret_cast<u32x4*>(q) + p * nblk + b, pv);
+          scales[p * nblk + b] = sbyte;
+        }
       }
     }
     if constexpr (K == 0) __syncthreads();  // s_pos is rewritten for the next token
@@ -229,11 +241,22 @@ struct LaunchBf16 {
 
 template <int K>
 struct LaunchMxfp4 {
-  static hipError_t run(const u32x4* x, int64_t n_rows, int h16, int top_k, const uint32_t* restore,
-                        u32x4* q, uint8_t* scales, uint32_t limit, hipStream_t s) {
-    hipLaunchKernelGGL(k_dispatch_mxfp4<K>, dim3(row_grid(n_rows)), dim3(kMxThreads), 0, s, x,
-                       n_rows, h16, top_k, restore, q, scales, limit);
+  template <bool kEven, bool kPacked>
+  static hipError_t go(const u32x4* x, int64_t n_rows, int h16, int top_k,
+                       const uint32_t* restore, uint8_t* q, uint8_t* scales, uint32_t limit,
+                       hipStream_t s) {
+    hipLaunchKernelGGL((k_dispatch_mxfp4<K, kEven, kPacked>), dim3(row_grid(n_rows)),
+                       dim3(kMxThreads), 0, s, x, n_rows, h16, top_k, restore, q, scales, limit);
     return hipGetLastError();
+  }
+  static hipError_t run(const u32x4* x, int64_t n_rows, int h16, int top_k, const uint32_t* restore,
+                        uint8_t* q, uint8_t* scales, uint32_t limit, int mode, hipStream_t s) {
+    switch (mode) {
+      case 0: return go<false, false>(x, n_rows, h16, top_k, restore, q, scales, limit, s);
+      case 1: return go<true, false>(x, n_rows, h16, top_k, restore, q, scales, limit, s);
+      case 2: return go<false, true>(x, n_rows, h16, top_k, restore, q, scales, limit, s);
+      default: return go<true, true>(x, n_rows, h16, top_k, restore, q, scales, limit, s);
+    }
   }
 };
 
@@ -249,11 +272,11 @@ hipError_t launch_dispatch_bf16(const uint16_t* x, int64_t n_rows, int hidden, i
 
 hipError_t launch_dispatch_mxfp4(const uint16_t* x, int64_t n_rows, int hidden, int top_k,
                                  const uint32_t* restore, uint8_t* q, uint8_t* scales,
-                                 int64_t out_rows, hipStream_t s) {
+                                 int64_t out_rows, bool even_scale, bool packed, hipStream_t s) {
   if (n_rows == 0) return hipSuccess;
+  const int mode = (even_scale ? 1 : 0) | (packed ? 2 : 0);
   return by_top_k<LaunchMxfp4>(top_k, reinterpret_cast<const u32x4*>(x), n_rows, hidden / 8, top_k,
-                               restore, reinterpret_cast<u32x4*>(q), scales,
-                               position_limit(out_rows), s);
+                               restore, q, scales, position_limit(out_rows), mode, s);
 }
 
 }  // namespace moe

@@ -36,12 +36,17 @@ __device__ __forceinline__ uint32_t bucket_of(int32_t id, uint32_t n_experts) {
   return uint32_t(id) < n_experts ? uint32_t(id) : n_experts;
 }
 
+__device__ __forceinline__ uint32_t bucket_of(int64_t id, uint32_t n_experts) {
+  return uint64_t(id) < uint64_t(n_experts) ? uint32_t(id) : n_experts;
+}
+
 __device__ __forceinline__ bool is_leader(uint64_t peers) {
   return peers != 0 && __builtin_ctzll(peers) == __lane_id();
 }
 
 // Count the chunk's slots per bucket into hist[0..E] (LDS, zeroed by caller).
-__device__ void chunk_histogram(const int32_t* __restrict__ ids, int64_t n_slots, int64_t begin,
+template <typename IdT>
+__device__ void chunk_histogram(const IdT* __restrict__ ids, int64_t n_slots, int64_t begin,
                                 uint32_t n_experts, int nbits, uint32_t* hist) {
   const int tid = threadIdx.x;
   uint32_t key[kIdxRounds];
@@ -63,7 +68,8 @@ __device__ void chunk_histogram(const int32_t* __restrict__ ids, int64_t n_slots
 // slot of bucket b.  whist is LDS scratch [kIdxWaves][E+1].  Wave w owns the
 // kIdxRounds*64 consecutive slots starting at begin + w*kIdxRounds*64, so the
 // slot order is wave-major, round, lane -- ascending slot index.
-__device__ void chunk_scatter(const int32_t* __restrict__ ids, int64_t n_slots, int64_t begin,
+template <typename IdT>
+__device__ void chunk_scatter(const IdT* __restrict__ ids, int64_t n_slots, int64_t begin,
                               uint32_t n_experts, int nbits, const uint32_t* off, uint32_t* whist,
                               uint32_t* __restrict__ teo, uint32_t* __restrict__ restore) {
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
@@ -115,46 +121,55 @@ __device__ void chunk_scatter(const int32_t* __restrict__ ids, int64_t n_slots, 
 }
 
 // Block-wide: from per-bucket totals tot[0..E] (LDS) write the bucket starts
-// base[0..E] (exclusive scan, base[E] = V) and the compacted CSR outputs.
+// base[0..E] (exclusive scan, base[E] = V) and the compacted CSR outputs;
+// with soff given, also the aligned offsets (exclusive scan over active
+// experts of their counts rounded up to `align`).
 __device__ void finalize_counts(const uint32_t* tot, uint32_t n_experts, uint32_t* base,
                                 uint32_t* __restrict__ esi, int32_t* __restrict__ expert_ids,
-                                uint32_t* __restrict__ stats) {
-  __shared__ uint32_t part[3 * kIdxWaves];
+                                uint32_t* __restrict__ stats, uint32_t* __restrict__ soff,
+                                uint32_t align) {
+  __shared__ uint32_t part[4 * kIdxWaves];
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
   const int nb = int(n_experts) + 1;
   const int ipt = (nb + kIdxThreads - 1) / kIdxThreads;
   const int b0 = tid * ipt;
-  uint32_t s_tot = 0, s_act = 0, s_max = 0;
+  const bool want_soff = soff != nullptr;
+  uint32_t s_tot = 0, s_act = 0, s_max = 0, s_al = 0;
   for (int q = 0; q < ipt; ++q) {
     const int b = b0 + q;
     if (b < nb) {
       const uint32_t v = tot[b];
       s_tot += v;
-      if (b < int(n_experts)) {
-        s_act += v > 0 ? 1u : 0u;
+      if (b < int(n_experts) && v > 0) {
+        s_act += 1u;
         s_max = max(s_max, v);
+        if (want_soff) s_al += (v + align - 1) / align * align;
       }
     }
   }
   const uint32_t in_tot = wave_inclusive_sum(s_tot);
   const uint32_t in_act = wave_inclusive_sum(s_act);
+  const uint32_t in_al = wave_inclusive_sum(s_al);
   const uint32_t w_max = wave_max(s_max);
   if (lane == kWave - 1) {
     part[wave] = in_tot;
     part[kIdxWaves + wave] = in_act;
     part[2 * kIdxWaves + wave] = w_max;
+    part[3 * kIdxWaves + wave] = in_al;
   }
   __syncthreads();
-  uint32_t p_tot = in_tot - s_tot, p_act = in_act - s_act;
-  uint32_t all_tot = 0, all_act = 0, all_max = 0;
+  uint32_t p_tot = in_tot - s_tot, p_act = in_act - s_act, p_al = in_al - s_al;
+  uint32_t all_tot = 0, all_act = 0, all_max = 0, all_al = 0;
   for (int w = 0; w < kIdxWaves; ++w) {
     if (w < wave) {
       p_tot += part[w];
       p_act += part[kIdxWaves + w];
+      p_al += part[3 * kIdxWaves + w];
     }
     all_tot += part[w];
     all_act += part[kIdxWaves + w];
     all_max = max(all_max, part[2 * kIdxWaves + w]);
+    all_al += part[3 * kIdxWaves + w];
   }
   for (int q = 0; q < ipt; ++q) {
     const int b = b0 + q;
@@ -164,6 +179,10 @@ __device__ void finalize_counts(const uint32_t* tot, uint32_t n_experts, uint32_
       if (b < int(n_experts) && v > 0) {
         expert_ids[p_act] = b;
         esi[p_act] = p_tot;
+        if (want_soff) {
+          soff[p_act] = p_al;
+          p_al += (v + align - 1) / align * align;
+        }
         ++p_act;
       }
       p_tot += v;
@@ -171,7 +190,10 @@ __device__ void finalize_counts(const uint32_t* tot, uint32_t n_experts, uint32_
   }
   const uint32_t n_routed = all_tot - tot[n_experts];
   for (uint32_t j = all_act + tid; j < n_experts; j += kIdxThreads) expert_ids[j] = -1;
-  for (uint32_t j = all_act + tid; j <= n_experts; j += kIdxThreads) esi[j] = n_routed;
+  for (uint32_t j = all_act + tid; j <= n_experts; j += kIdxThreads) {
+    esi[j] = n_routed;
+    if (want_soff) soff[j] = all_al;
+  }
   if (tid == 0) {
     stats[0] = all_max;
     stats[1] = all_act;
@@ -226,11 +248,12 @@ __global__ __launch_bounds__(256) void k_index_zero(IndexWorkspace ws, int64_t n
 
 // n_chunks == 1: one workgroup does histogram, scan and scatter.
 // n_chunks > 1: histogram + lookback + (last ticket) CSR outputs.
+template <typename IdT>
 __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
-    const int32_t* __restrict__ ids, int64_t n_slots, uint32_t n_experts, int nbits,
+    const IdT* __restrict__ ids, int64_t n_slots, uint32_t n_experts, int nbits,
     int64_t n_chunks, IndexWorkspace ws, uint32_t* __restrict__ esi,
-    int32_t* __restrict__ expert_ids, uint32_t* __restrict__ stats, uint32_t* __restrict__ teo,
-    uint32_t* __restrict__ restore) {
+    int32_t* __restrict__ expert_ids, uint32_t* __restrict__ stats, uint32_t* __restrict__ soff,
+    uint32_t align, uint32_t* __restrict__ teo, uint32_t* __restrict__ restore) {
   extern __shared__ uint32_t lds[];
   __shared__ int64_t s_chunk;
   const int nb = int(n_experts) + 1;
@@ -268,7 +291,7 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
 
   if (c == n_chunks - 1) {
     uint32_t* base = n_chunks > 1 ? ws.base : lds + nb;
-    finalize_counts(hist, n_experts, base, esi, expert_ids, stats);
+    finalize_counts(hist, n_experts, base, esi, expert_ids, stats, soff, align);
     if (n_chunks == 1) {
       __syncthreads();
       chunk_scatter(ids, n_slots, 0, n_experts, nbits, lds + nb, lds + 2 * nb, teo, restore);
@@ -276,8 +299,9 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
   }
 }
 
+template <typename IdT>
 __global__ __launch_bounds__(kIdxThreads) void k_index_scatter(
-    const int32_t* __restrict__ ids, int64_t n_slots, uint32_t n_experts, int nbits,
+    const IdT* __restrict__ ids, int64_t n_slots, uint32_t n_experts, int nbits,
     IndexWorkspace ws, uint32_t* __restrict__ teo, uint32_t* __restrict__ restore) {
   extern __shared__ uint32_t lds[];
   const int nb = int(n_experts) + 1;
@@ -312,17 +336,20 @@ IndexWorkspace index_workspace_carve(void* ws, int64_t n_slots, int n_experts) {
   return w;
 }
 
-hipError_t launch_create_indices(const int32_t* ids, int64_t n_slots, int n_experts,
-                                 uint32_t* teo, uint32_t* esi, uint32_t* restore,
-                                 int32_t* expert_ids, uint32_t* stats, void* wsp, hipStream_t s) {
+template <typename IdT>
+hipError_t launch_create_indices(const IdT* ids, int64_t n_slots, int n_experts, uint32_t* teo,
+                                 uint32_t* esi, uint32_t* restore, int32_t* expert_ids,
+                                 uint32_t* stats, uint32_t* soff, uint32_t align, void* wsp,
+                                 hipStream_t s) {
   const int64_t chunks = index_chunks(n_slots);
   const int nb = n_experts + 1;
   const int nbits = 32 - __builtin_clz(uint32_t(n_experts));
   const IndexWorkspace ws = index_workspace_carve(wsp, n_slots, n_experts);
   if (chunks == 1) {
     const size_t lds = size_t(2 + kIdxWaves) * nb * sizeof(uint32_t);
-    hipLaunchKernelGGL(k_index_hist, dim3(1), dim3(kIdxThreads), lds, s, ids, n_slots,
-                       uint32_t(n_experts), nbits, chunks, ws, esi, expert_ids, stats, teo, restore);
+    hipLaunchKernelGGL(k_index_hist<IdT>, dim3(1), dim3(kIdxThreads), lds, s, ids, n_slots,
+                       uint32_t(n_experts), nbits, chunks, ws, esi, expert_ids, stats, soff, align,
+                       teo, restore);
     return hipGetLastError();
   }
   const int64_t n_flags = chunks * nb;
@@ -330,15 +357,22 @@ hipError_t launch_create_indices(const int32_t* ids, int64_t n_slots, int n_expe
                      n_flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_index_hist, dim3(uint32_t(chunks)), dim3(kIdxThreads),
+  hipLaunchKernelGGL(k_index_hist<IdT>, dim3(uint32_t(chunks)), dim3(kIdxThreads),
                      size_t(nb) * sizeof(uint32_t), s, ids, n_slots, uint32_t(n_experts), nbits,
-                     chunks, ws, esi, expert_ids, stats, teo, restore);
+                     chunks, ws, esi, expert_ids, stats, soff, align, teo, restore);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_index_scatter, dim3(uint32_t(chunks)), dim3(kIdxThreads),
+  hipLaunchKernelGGL(k_index_scatter<IdT>, dim3(uint32_t(chunks)), dim3(kIdxThreads),
                      size_t(1 + kIdxWaves) * nb * sizeof(uint32_t), s, ids, n_slots,
                      uint32_t(n_experts), nbits, ws, teo, restore);
   return hipGetLastError();
 }
+
+template hipError_t launch_create_indices<int32_t>(const int32_t*, int64_t, int, uint32_t*,
+                                                   uint32_t*, uint32_t*, int32_t*, uint32_t*,
+                                                   uint32_t*, uint32_t, void*, hipStream_t);
+template hipError_t launch_create_indices<int64_t>(const int64_t*, int64_t, int, uint32_t*,
+                                                   uint32_t*, uint32_t*, int32_t*, uint32_t*,
+                                                   uint32_t*, uint32_t, void*, hipStream_t);
 
 }  // namespace moe

@@ -34,12 +34,15 @@ int64_t index_chunks(int64_t n_slots);
 size_t index_workspace_bytes(int64_t n_slots, int n_experts);
 IndexWorkspace index_workspace_carve(void* ws, int64_t n_slots, int n_experts);
 
-hipError_t launch_mask_padding(int32_t* ids, int64_t n_rows, int top_k, const int32_t* count,
+template <typename IdT>
+hipError_t launch_mask_padding(IdT* ids, int64_t n_rows, int top_k, const int32_t* count,
                                int tp_rank, hipStream_t s);
 
-hipError_t launch_create_indices(const int32_t* ids, int64_t n_slots, int n_experts,
-                                 uint32_t* teo, uint32_t* esi, uint32_t* restore,
-                                 int32_t* expert_ids, uint32_t* stats, void* ws, hipStream_t s);
+template <typename IdT>
+hipError_t launch_create_indices(const IdT* ids, int64_t n_slots, int n_experts, uint32_t* teo,
+                                 uint32_t* esi, uint32_t* restore, int32_t* expert_ids,
+                                 uint32_t* stats, uint32_t* scales_offset, uint32_t scales_align,
+                                 void* ws, hipStream_t s);
 
 hipError_t launch_dispatch_bf16(const uint16_t* x, int64_t n_rows, int hidden, int top_k,
                                 const uint32_t* restore, uint16_t* out, int64_t out_rows,
@@ -47,10 +50,12 @@ hipError_t launch_dispatch_bf16(const uint16_t* x, int64_t n_rows, int hidden, i
 
 hipError_t launch_dispatch_mxfp4(const uint16_t* x, int64_t n_rows, int hidden, int top_k,
                                  const uint32_t* restore, uint8_t* q, uint8_t* scales,
-                                 int64_t out_rows, hipStream_t s);
+                                 int64_t out_rows, bool even_scale, bool packed, hipStream_t s);
 
+// scale / residual: the fused epilogue (epilogue = false keeps the plain sum).
 hipError_t launch_combine(const uint16_t* y, int64_t y_rows, const float* w,
                           const uint32_t* restore, int64_t n_rows, int hidden, int top_k,
-                          uint16_t* out, hipStream_t s);
+                          bool epilogue, float scale, const uint16_t* residual, uint16_t* out,
+                          hipStream_t s);
 
 }  // namespace moe

@@ -44,6 +44,10 @@ extern "C" {
 #define MOE_MAX_TOP_K 1024
 #define MOE_MXFP4_BLOCK 32
 
+/* moe_dispatch_mxfp4 flags */
+#define MOE_MXFP4_EVEN_SCALE 1u  /* "even-mode" scale exponent (see moe_dispatch_mxfp4) */
+#define MOE_MXFP4_PACKED_ROWS 2u /* payload and scales packed into one row per slot */
+
 typedef enum moe_status {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARGUMENT = 1,
@@ -77,6 +81,13 @@ int moe_mask_padding(int32_t* routing_map, int64_t n_rows, int32_t top_k,
                      const int32_t* real_token_count, int32_t tp_rank, void* stream);
 
 /*
+ * As moe_mask_padding for an int64 routing map [n_rows, top_k] (the dtype of
+ * the routing map on the mask page's mask_routing_padding parameters).
+ */
+int moe_mask_padding_i64(int64_t* routing_map, int64_t n_rows, int32_t top_k,
+                         const int32_t* real_token_count, int32_t tp_rank, void* stream);
+
+/*
  * Size in bytes of the scratch workspace moe_create_indices needs for
  * n_slots slots and n_experts experts (0 if the sizes are out of range). [host]
  */
@@ -107,6 +118,15 @@ size_t moe_create_indices_workspace_bytes(int64_t n_slots, int32_t n_experts);
  *                         ascending order, then -1.
  *   expert_usage_stats    [device] uint32 [2] out: {largest number of slots
  *                         on one expert, number of active experts A}.
+ *   scales_offset         [device] uint32 [E+1] out, or NULL ("moe_create_indices",
+ *                         Args: scales_offset_p, the aligned scale offsets for
+ *                         block-scaled grouped matmul): entry j < A is the sum over
+ *                         active experts j' < j of their slot count rounded up
+ *                         to a multiple of scales_align; entries A..E hold the
+ *                         total.  Offsets are in rows; a block-scaled GEMM
+ *                         multiplies by its bytes per scale row.
+ *   scales_align          >= 1 when scales_offset is given (ignored otherwise);
+ *                         S + E*scales_align must stay below 2^32.
  *   workspace             [device] scratch of at least
  *                         moe_create_indices_workspace_bytes(S, E) bytes,
  *                         256-byte aligned, no initial contents required.
@@ -116,8 +136,17 @@ size_t moe_create_indices_workspace_bytes(int64_t n_slots, int32_t n_experts);
 int moe_create_indices(const int32_t* topk_ids, int64_t n_slots, int32_t n_experts,
                        uint32_t* token_expert_order, uint32_t* expert_start_indices,
                        uint32_t* restore_token_order, int32_t* expert_ids,
-                       uint32_t* expert_usage_stats, void* workspace, size_t workspace_bytes,
+                       uint32_t* expert_usage_stats, uint32_t* scales_offset,
+                       uint32_t scales_align, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/* As moe_create_indices for int64 expert ids (topk_ids [n_slots] int64). */
+int moe_create_indices_i64(const int64_t* topk_ids, int64_t n_slots, int32_t n_experts,
+                           uint32_t* token_expert_order, uint32_t* expert_start_indices,
+                           uint32_t* restore_token_order, int32_t* expert_ids,
+                           uint32_t* expert_usage_stats, uint32_t* scales_offset,
+                           uint32_t scales_align, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /*
  * Stage 3a -- dispatch in bf16.
@@ -149,6 +178,12 @@ int moe_dispatch(const uint16_t* input_tokens, int64_t n_rows, int32_t hidden, i
  * position the row's slots map to:
  *   scale exponent  se = clamp(floor(log2(max |x|)) - 2, -127, 127),
  *                   se = -127 for an all-zero block; stored as se + 127.
+ *                   With MOE_MXFP4_EVEN_SCALE (the page's "per-token
+ *                   even-mode scales", read as: round max |x| to E2M1's one
+ *                   mantissa bit, halves up, before the floor):
+ *                   floor(log2(max |x|)) gains 1 when the mantissa fraction
+ *                   of max |x| is >= 0.75, so a block maximum that would
+ *                   scale into [7, 8) lands in [3.5, 4) instead.
  *   element code    nearest of {0, .5, 1, 1.5, 2, 3, 4, 6} to |x| * 2^-se,
  *                   ties to the even code, values above 6 saturate to 6;
  *                   bit 3 = sign bit of x (kept on zero).
@@ -156,10 +191,14 @@ int moe_dispatch(const uint16_t* input_tokens, int64_t n_rows, int32_t hidden, i
  * Inputs must be finite.
  *
  *   input_tokens, n_rows, top_k, restore_token_order  as moe_dispatch.
- *   hidden        > 0, a multiple of 32.
- *   out_q         [device] uint8 [out_rows, hidden/2], 16-byte aligned.
- *   out_scales    [device] uint8 [out_rows, hidden/32].
- *   flags         must be 0 (the scale rule above).
+ *   hidden        > 0, a multiple of 32 (of 512 with MOE_MXFP4_PACKED_ROWS).
+ *   out_q         [device] uint8 [out_rows, hidden/2], 16-byte aligned; with
+ *                 MOE_MXFP4_PACKED_ROWS uint8 [out_rows, hidden/2 + hidden/32]
+ *                 holding each slot's payload followed by its scale bytes
+ *                 (the page's scales "packed alongside the FP4 quants").
+ *   out_scales    [device] uint8 [out_rows, hidden/32]; NULL with
+ *                 MOE_MXFP4_PACKED_ROWS.
+ *   flags         0, or an OR of MOE_MXFP4_EVEN_SCALE and MOE_MXFP4_PACKED_ROWS.
  */
 int moe_dispatch_mxfp4(const uint16_t* input_tokens, int64_t n_rows, int32_t hidden,
                        int32_t top_k, const uint32_t* restore_token_order, uint8_t* out_q,
@@ -187,6 +226,23 @@ int moe_dispatch_mxfp4(const uint16_t* input_tokens, int64_t n_rows, int32_t hid
 int moe_combine(const uint16_t* y, int64_t y_rows, const float* router_weights,
                 const uint32_t* restore_token_order, int64_t n_rows, int32_t hidden,
                 int32_t top_k, uint16_t* output_tokens, void* stream);
+
+/*
+ * Combine with an elementwise epilogue fused in ("Struct_ep_combine_wait",
+ * Parameters: has_epilogue_fusion applies an elementwise function after the
+ * weighted sum).  The epilogue here is a scale and an optional residual add:
+ *   out[t] = bf16( fl(fl(scale * acc[t]) + residual[t]) )     (residual given)
+ *   out[t] = bf16( fl(scale * acc[t]) )                       (residual NULL)
+ * with acc[t] the fp32 sum of moe_combine, every operation rounded on its
+ * own.  scale = 1 and residual = NULL give exactly moe_combine.
+ *   residual      [device] bf16 [n_rows, hidden], 16-byte aligned, or NULL;
+ *                 must not overlap output_tokens.
+ * Other arguments as moe_combine.
+ */
+int moe_combine_epilogue(const uint16_t* y, int64_t y_rows, const float* router_weights,
+                         const uint32_t* restore_token_order, int64_t n_rows, int32_t hidden,
+                         int32_t top_k, float scale, const uint16_t* residual,
+                         uint16_t* output_tokens, void* stream);
 
 #ifdef __cplusplus
 }

@@ -7,6 +7,7 @@ from .moe_oracle import (  # noqa: F401
     SENT,
     bf16_bits_to_f32,
     combine,
+    combine_epilogue,
     create_indices,
     dispatch,
     dispatch_mxfp4,

@@ -28,6 +28,9 @@ Readings taken where the pages are silent (each also listed in the design doc):
   * expert_ids / expert_start_indices are compacted over the experts that
     received at least one slot; unused tails hold -1 / the routed count V.
   * expert_usage_stats = [max slots on one expert, number of active experts].
+  * scales_offset (optional): for active expert j, the sum over earlier
+    active experts of their slot count rounded up to a multiple of
+    scales_align; entries from the active count on hold the total.
   * unused entries of token_expert_order and restore_token_order hold
     0xFFFFFFFF.
   * MXFP4: blocks of 32 elements along the hidden dimension, E2M1 payload
@@ -37,6 +40,11 @@ Readings taken where the pages are silent (each also listed in the design doc):
     |v| * 2**-exponent, ties to the even code, saturating at 6; the sign bit
     is kept (also on zero).  Element 2m in the low nibble of byte m.
     Non-finite inputs are outside the pinned domain (parity unpinned there).
+    "Even-mode" scale: max |v| is first rounded to E2M1's one mantissa bit,
+    halves up, so floor(log2) gains 1 when its mantissa fraction is >= 0.75.
+    Packed rows: each slot's H/2 payload bytes followed by its H/32 scales.
+  * combine epilogue: out = bf16(fl(fl(scale * acc) + residual)), residual
+    optional, each operation rounded on its own.
   * combine: fp32, acc = +0, then for j = 0..top_k-1 in order and only for
     routed slots, acc = fl(acc + fl(w[t,j] * y[pos])) with every operation
     rounded on its own (no fused multiply-add); output = bf16 round to
@@ -88,11 +96,12 @@ def mask_routing_padding(routing_map: np.ndarray, real_token_count: int, tp_rank
 # --------------------------------------------------------------------------
 # stage 2: expert-grouped indices
 # --------------------------------------------------------------------------
-def create_indices(topk_ids: np.ndarray, n_experts: int) -> dict:
+def create_indices(topk_ids: np.ndarray, n_experts: int, scales_align: int = None) -> dict:
     """Group routed slots by expert ("moe_create_indices", description and Args).
 
     Histogram of expert ids -> CSR starts over the active experts -> stable
-    scatter of slot indices, with its inverse."""
+    scatter of slot indices, with its inverse.  With scales_align, also the
+    aligned scale offsets (Args: scales_offset_p)."""
     f = np.asarray(topk_ids).reshape(-1).astype(np.int64)
     n_slots = f.size
     routed = (f >= 0) & (f < n_experts)
@@ -118,12 +127,19 @@ def create_indices(topk_ids: np.ndarray, n_experts: int) -> dict:
     restore_token_order = np.full(n_slots, SENT, dtype=np.uint32)
     restore_token_order[order[:n_routed]] = np.arange(n_routed, dtype=np.uint32)
 
-    return dict(token_expert_order=token_expert_order,
-                expert_start_indices=expert_start_indices,
-                restore_token_order=restore_token_order,
-                expert_ids=expert_ids,
-                expert_usage_stats=expert_usage_stats,
-                n_routed=n_routed)
+    out = dict(token_expert_order=token_expert_order,
+               expert_start_indices=expert_start_indices,
+               restore_token_order=restore_token_order,
+               expert_ids=expert_ids,
+               expert_usage_stats=expert_usage_stats,
+               n_routed=n_routed)
+    if scales_align is not None:
+        padded = -(-counts[active] // scales_align) * scales_align
+        total = int(padded.sum())
+        scales_offset = np.full(n_experts + 1, total, dtype=np.uint32)
+        scales_offset[:n_active] = np.concatenate([[0], np.cumsum(padded)[:-1]]) if n_active else []
+        out["scales_offset"] = scales_offset
+    return out
 
 
 # --------------------------------------------------------------------------
@@ -140,7 +156,7 @@ def dispatch(input_tokens: np.ndarray, token_expert_order: np.ndarray, top_k: in
 # --------------------------------------------------------------------------
 # stage 3b: dispatch, MXFP4
 # --------------------------------------------------------------------------
-def mxfp4_quantize(x_bits: np.ndarray):
+def mxfp4_quantize(x_bits: np.ndarray, even: bool = False):
     """MXFP4 encoding of bf16 rows [T, H] -> (payload uint8 [T, H/2], scales uint8 [T, H/32]).
 
     ("Struct_ep_dispatch_async_mxfp4": FP4 quants with scales; block of 32,
@@ -154,8 +170,10 @@ def mxfp4_quantize(x_bits: np.ndarray):
     v = bf16_bits_to_f32(x_bits).astype(np.float64).reshape(t, nb, MX_BLOCK)
 
     amax = np.abs(v).max(axis=2)
-    _, e = np.frexp(amax)                   # amax = m * 2**e with m in [0.5, 1)
+    m, e = np.frexp(amax)                   # amax = m * 2**e with m in [0.5, 1)
     floor_log2 = e.astype(np.int64) - 1
+    if even:                                # mantissa fraction 2m - 1 >= 0.75 rounds up a binade
+        floor_log2 = floor_log2 + (m >= 0.875)
     se = np.where(amax > 0, np.clip(floor_log2 - E2M1_EMAX, -127, 127), -127)
 
     s = np.abs(v) * np.ldexp(1.0, -se)[:, :, None]
@@ -186,21 +204,41 @@ def mxfp4_dequantize(payload: np.ndarray, scales: np.ndarray) -> np.ndarray:
 
 
 def dispatch_mxfp4(input_tokens: np.ndarray, token_expert_order: np.ndarray, top_k: int, n_routed: int,
-                   rows_per_pass: int = 64):
-    """Row p of the result is the MXFP4 encoding of input_tokens[teo[p] // top_k]."""
+                   rows_per_pass: int = 64, even: bool = False, packed: bool = False):
+    """Row p of the result is the MXFP4 encoding of input_tokens[teo[p] // top_k].
+
+    Returns (payload, scales), or with packed=True one array whose rows are
+    payload followed by scales."""
     src = token_expert_order[:n_routed].astype(np.int64) // top_k
     h = input_tokens.shape[1]
     payload = np.empty((n_routed, h // 2), dtype=np.uint8)
     scales = np.empty((n_routed, h // MX_BLOCK), dtype=np.uint8)
     for p0 in range(0, n_routed, rows_per_pass):
         p1 = min(n_routed, p0 + rows_per_pass)
-        payload[p0:p1], scales[p0:p1] = mxfp4_quantize(np.asarray(input_tokens)[src[p0:p1]])
+        payload[p0:p1], scales[p0:p1] = mxfp4_quantize(np.asarray(input_tokens)[src[p0:p1]], even)
+    if packed:
+        return np.concatenate([payload, scales], axis=1)
     return payload, scales
 
 
 # --------------------------------------------------------------------------
 # stage 4: combine
 # --------------------------------------------------------------------------
+def _combine_acc(y_bits, w, pos, t0, t1, top_k):
+    """fp32 sum for rows [t0, t1): acc = +0, then acc = fl(acc + fl(w*y)) over routed j ascending."""
+    h = y_bits.shape[1]
+    acc = np.zeros((t1 - t0, h), dtype=np.float32)
+    for j in range(top_k):
+        p = pos[t0:t1, j]
+        routed = p != SENT
+        if not routed.any():
+            continue
+        rows = bf16_bits_to_f32(y_bits[np.where(routed, p, 0).astype(np.int64)])
+        prod = w[t0:t1, j, None] * rows            # one fp32 rounding
+        acc = np.where(routed[:, None], acc + prod, acc)   # one fp32 rounding
+    return acc
+
+
 def combine(y_bits: np.ndarray, router_weights: np.ndarray, restore_token_order: np.ndarray,
             top_k: int, rows_per_pass: int = 256) -> np.ndarray:
     """out[t] = bf16( sum over j = 0..top_k-1 of w[t,j] * y[restore[t*top_k + j]] ).
@@ -208,6 +246,15 @@ def combine(y_bits: np.ndarray, router_weights: np.ndarray, restore_token_order:
     ("Struct_ep_combine_wait": weighted sum of routed expert outputs with the
     router weights, output [num_tokens, hidden_size].)  fp32 with each product
     and each sum rounded separately, j ascending, unrouted slots skipped."""
+    return combine_epilogue(y_bits, router_weights, restore_token_order, top_k, None, None, rows_per_pass)
+
+
+def combine_epilogue(y_bits: np.ndarray, router_weights: np.ndarray, restore_token_order: np.ndarray,
+                     top_k: int, scale=1.0, residual_bits: np.ndarray = None,
+                     rows_per_pass: int = 256) -> np.ndarray:
+    """combine followed by the fused elementwise epilogue ("Struct_ep_combine_wait",
+    Parameters: has_epilogue_fusion): out = bf16(fl(fl(scale * acc) + residual)).
+    scale=None and residual=None give the plain combine."""
     w = np.asarray(router_weights, dtype=np.float32)
     n = w.shape[0]
     pos = np.asarray(restore_token_order, dtype=np.uint32).reshape(n, top_k)
@@ -216,14 +263,10 @@ def combine(y_bits: np.ndarray, router_weights: np.ndarray, restore_token_order:
     out = np.empty((n, h), dtype=np.uint16)
     for t0 in range(0, n, rows_per_pass):
         t1 = min(n, t0 + rows_per_pass)
-        acc = np.zeros((t1 - t0, h), dtype=np.float32)
-        for j in range(top_k):
-            p = pos[t0:t1, j]
-            routed = p != SENT
-            if not routed.any():
-                continue
-            rows = bf16_bits_to_f32(y_bits[np.where(routed, p, 0).astype(np.int64)])
-            prod = w[t0:t1, j, None] * rows            # one fp32 rounding
-            acc = np.where(routed[:, None], acc + prod, acc)   # one fp32 rounding
+        acc = _combine_acc(y_bits, w, pos, t0, t1, top_k)
+        if scale is not None:
+            acc = np.float32(scale) * acc                              # one fp32 rounding
+        if residual_bits is not None:
+            acc = acc + bf16_bits_to_f32(np.asarray(residual_bits)[t0:t1])   # one fp32 rounding
         out[t0:t1] = f32_to_bf16_rne(acc)
     return out

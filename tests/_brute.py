@@ -145,3 +145,65 @@ def combine_row(weights_row, y_rows, positions):
             acc = f32(acc + prod)
         out.append(bf16(acc))
     return out
+
+
+# ---------------------------------------------------------------- next rows
+def scales_offset(flat_ids, n_experts, align):
+    """Walk the experts in id order; each active one starts at the running
+    total, which then grows by its count rounded up to `align`."""
+    counts = [0] * n_experts
+    for f in flat_ids:
+        if 0 <= f < n_experts:
+            counts[f] += 1
+    out, run = [], 0
+    for e in range(n_experts):
+        if counts[e] > 0:
+            out.append(run)
+            c = counts[e]
+            while c % align:
+                c += 1
+            run += c
+    return out + [run] * (n_experts + 1 - len(out))
+
+
+def even_scale_byte(bits32):
+    """Scale byte under the even-mode rule: round max |x| to one mantissa bit
+    (halves up) and take floor(log2) of the rounded value."""
+    amax = max(abs(bf16_value(b)[0]) for b in bits32)
+    if amax == 0:
+        return 0
+    e = floor_log2(amax)
+    unit = Fraction(2) ** (e - 1)            # one mantissa bit below the leading bit
+    n = amax / unit
+    q = n.numerator // n.denominator
+    if n - q >= Fraction(1, 2):
+        q += 1
+    rounded = q * unit
+    se = min(max(floor_log2(rounded) - 2, -127), 127)
+    return se + 127
+
+
+def combine_epilogue_row(weights_row, y_rows, positions, scale, residual_row):
+    plain = combine_row_f32(weights_row, y_rows, positions)
+    out = []
+    for c, acc in enumerate(plain):
+        r = f32(Fraction(float(scale)) * acc) if scale is not None else acc
+        if residual_row is not None:
+            r = f32(r + bf16_value(residual_row[c])[0])
+        out.append(bf16(r))
+    return out
+
+
+def combine_row_f32(weights_row, y_rows, positions):
+    h = len(y_rows[0]) if y_rows else 0
+    out = []
+    for c in range(h):
+        acc = Fraction(0)
+        for j, p in enumerate(positions):
+            if p == SENT:
+                continue
+            w = Fraction(float(weights_row[j]))
+            y, _ = bf16_value(y_rows[p][c])
+            acc = f32(acc + f32(w * y))
+        out.append(acc)
+    return out

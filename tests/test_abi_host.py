@@ -24,8 +24,9 @@ def declared_functions():
 
 def test_header_declares_the_path():
     assert declared_functions() == sorted([
-        "moe_error_string", "moe_mask_padding", "moe_create_indices_workspace_bytes",
-        "moe_create_indices", "moe_dispatch", "moe_dispatch_mxfp4", "moe_combine"])
+        "moe_error_string", "moe_mask_padding", "moe_mask_padding_i64", "moe_create_indices_workspace_bytes",
+        "moe_create_indices", "moe_create_indices_i64", "moe_dispatch", "moe_dispatch_mxfp4", "moe_combine",
+        "moe_combine_epilogue"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -69,23 +70,35 @@ def test_invalid_arguments_rejected_on_host():
     assert L.moe_mask_padding(fake, -1, 2, cnt, 0, None) == 1         # n_rows < 0
     assert L.moe_mask_padding(fake, 2 ** 31, 2, cnt, 0, None) == 1    # slots reach the sentinel
     ws = mod.moe_create_indices_workspace_bytes(100, 8)
-    args = [fake, 100, 8, fake, fake, fake, fake, fake, fake, ws, None]
-    bad = list(args); bad[2] = 0
-    assert L.moe_create_indices(*bad) == 1                          # n_experts < 1
-    bad = list(args); bad[2] = 1025
-    assert L.moe_create_indices(*bad) == 1                          # n_experts too large
-    bad = list(args); bad[8] = None
-    assert L.moe_create_indices(*bad) == 1                          # null workspace
-    bad = list(args); bad[8] = P(256 + 8)
-    assert L.moe_create_indices(*bad) == 1                          # misaligned workspace
-    bad = list(args); bad[9] = ws - 1
-    assert L.moe_create_indices(*bad) == 2                          # workspace too small
+    args = [fake, 100, 8, fake, fake, fake, fake, fake, None, 0, fake, ws, None]
+    for fn in (L.moe_create_indices, L.moe_create_indices_i64):
+        bad = list(args); bad[2] = 0
+        assert fn(*bad) == 1                                        # n_experts < 1
+        bad = list(args); bad[2] = 1025
+        assert fn(*bad) == 1                                        # n_experts too large
+        bad = list(args); bad[10] = None
+        assert fn(*bad) == 1                                        # null workspace
+        bad = list(args); bad[10] = P(256 + 8)
+        assert fn(*bad) == 1                                        # misaligned workspace
+        bad = list(args); bad[11] = ws - 1
+        assert fn(*bad) == 2                                        # workspace too small
+        bad = list(args); bad[8] = fake; bad[9] = 0
+        assert fn(*bad) == 1                                        # scales_offset with align 0
+        bad = list(args); bad[8] = fake; bad[9] = 2 ** 31
+        assert fn(*bad) == 1                                        # aligned offsets would overflow
+    assert L.moe_mask_padding_i64(P(260), 4, 2, cnt, 0, None) == 1   # int64 map misaligned
     assert L.moe_dispatch(fake, 10, 12, 2, fake, fake, 20, None) == 1        # hidden % 8
     assert L.moe_dispatch(P(258), 10, 16, 2, fake, fake, 20, None) == 1      # misaligned x
     assert L.moe_dispatch(fake, 10, 16, 0, fake, fake, 20, None) == 1        # top_k < 1
     assert L.moe_dispatch(fake, 10, 16, 1025, fake, fake, 20, None) == 1     # top_k too large
     assert L.moe_dispatch_mxfp4(fake, 10, 48, 2, fake, fake, fake, 20, 0, None) == 1  # hidden % 32
-    assert L.moe_dispatch_mxfp4(fake, 10, 64, 2, fake, fake, fake, 20, 1, None) == 1  # flags
+    assert L.moe_dispatch_mxfp4(fake, 10, 64, 2, fake, fake, fake, 20, 4, None) == 1  # unknown flag
+    assert L.moe_dispatch_mxfp4(fake, 10, 256, 2, fake, fake, None, 20, 2, None) == 1  # packed: hidden % 512
+    assert L.moe_dispatch_mxfp4(fake, 10, 512, 2, fake, fake, fake, 20, 2, None) == 1  # packed: scales given
+    assert L.moe_dispatch_mxfp4(fake, 10, 512, 2, fake, fake, None, 20, 0, None) == 1  # unpacked: no scales
     assert L.moe_combine(fake, 20, fake, fake, 10, 12, 2, fake, None) == 1   # hidden % 8
     assert L.moe_combine(fake, 20, None, fake, 10, 16, 2, fake, None) == 1   # null weights
     assert L.moe_combine(fake, -1, fake, fake, 10, 16, 2, fake, None) == 1   # y_rows < 0
+    E = L.moe_combine_epilogue
+    assert E(fake, 20, fake, fake, 10, 16, 2, ctypes.c_float(1.0), P(264), fake, None) == 1  # residual misaligned
+    assert E(fake, 20, fake, fake, 10, 16, 2, ctypes.c_float(1.0), P(256 + 160), P(256), None) == 1  # overlap

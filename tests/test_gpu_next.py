@@ -1,0 +1,175 @@
+"""GPU parity of the extensions: aligned scale offsets, int64 routing maps,
+even-mode and packed MXFP4 dispatch, and the fused combine epilogue."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_common import SENT, bf16_from_bits, check_indices, gpu_available, i32, u16, u32
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+mod = pytest.importorskip("expert_grouping_dispatch_amd") if gpu_available() else None
+DEV = "cuda"
+
+
+def _indices(d_ids, e, align=None):
+    s = d_ids.numel()
+    idx = mod.alloc_indices(s, e, DEV, scales_offset=align is not None)
+    mod.moe_create_indices(d_ids, e, idx["token_expert_order"], idx["expert_start_indices"],
+                           idx["restore_token_order"], idx["expert_ids"], idx["expert_usage_stats"],
+                           idx["workspace"], idx["scales_offset"], align or 1)
+    torch.cuda.synchronize()
+    return idx
+
+
+@pytest.mark.parametrize("cfg", range(len(workloads.WORKLOADS)))
+@pytest.mark.parametrize("align", [1, 16, 128, 1000])
+def test_scales_offset_on_workloads(cfg, align):
+    w = workloads.WORKLOADS[cfg]
+    ids, _, real = workloads.make_routing(w, cfg)
+    m = oracle.mask_routing_padding(ids, real)
+    idx = _indices(torch.from_numpy(m).to(DEV), w.n_experts, align)
+    ref = oracle.create_indices(m, w.n_experts, scales_align=align)
+    check_indices(idx, ref)
+    np.testing.assert_array_equal(u32(idx["scales_offset"]), ref["scales_offset"])
+
+
+@pytest.mark.parametrize("n,k,e", [(0, 4, 16), (50, 3, 1), (1000, 8, 1024), (20000, 8, 256)])
+def test_scales_offset_edges(n, k, e):
+    g = np.random.default_rng(n + e)
+    ids = g.integers(-3, e + 3, size=(n, k)).astype(np.int32)
+    idx = _indices(torch.from_numpy(ids).to(DEV), e, 64)
+    ref = oracle.create_indices(ids, e, scales_align=64)
+    check_indices(idx, ref)
+    np.testing.assert_array_equal(u32(idx["scales_offset"]), ref["scales_offset"])
+
+
+@pytest.mark.parametrize("n,k,e,real", [(300, 4, 16, 211), (20000, 8, 256, 17000), (2, 2, 3, 5)])
+def test_int64_routing_map(n, k, e, real):
+    g = np.random.default_rng(n)
+    pool = np.array([-1, -(2 ** 40), 2 ** 31, 2 ** 33 + 1, e, -5] + list(range(e)), np.int64)
+    ids = g.choice(pool, size=(n, k))
+    d_ids = torch.from_numpy(ids).to(DEV)
+    cnt = torch.tensor([real], dtype=torch.int32, device=DEV)
+    mod.moe_mask_padding(d_ids, cnt, 0)
+    m = oracle.mask_routing_padding(ids, real)
+    np.testing.assert_array_equal(d_ids.cpu().numpy(), m)
+    idx = _indices(d_ids, e, 32)
+    ref = oracle.create_indices(m, e, scales_align=32)
+    check_indices(idx, ref)
+    np.testing.assert_array_equal(u32(idx["scales_offset"]), ref["scales_offset"])
+
+
+def _mxfp4_case(xb, ids, e, k, flags):
+    n, h = xb.shape
+    x = bf16_from_bits(xb, DEV)
+    ref = oracle.create_indices(ids, e)
+    restore = torch.from_numpy(ref["restore_token_order"].view(np.int32)).to(DEV).view(torch.uint32)
+    packed = bool(flags & mod.MXFP4_PACKED_ROWS)
+    q, sc = mod.alloc_dispatch_mxfp4(n * k, h, DEV, packed=packed)
+    mod.moe_dispatch_mxfp4(x, k, restore, q, sc, flags=flags)
+    torch.cuda.synchronize()
+    v = ref["n_routed"]
+    want = oracle.dispatch_mxfp4(xb, ref["token_expert_order"], k, v,
+                                 even=bool(flags & mod.MXFP4_EVEN_SCALE), packed=packed)
+    if packed:
+        np.testing.assert_array_equal(q[:v].cpu().numpy(), want)
+    else:
+        np.testing.assert_array_equal(q[:v].cpu().numpy(), want[0])
+        np.testing.assert_array_equal(sc[:v].cpu().numpy(), want[1])
+
+
+@pytest.mark.parametrize("flags", [1, 2, 3])
+def test_mxfp4_modes_on_decode_workload(flags):
+    w = workloads.WORKLOADS[3]
+    ids, _, real = workloads.make_routing(w, 3)
+    x, _ = workloads.make_dense(w, 3, DEV, y_rows=1)
+    _mxfp4_case(u16(x), oracle.mask_routing_padding(ids, real), w.n_experts, w.top_k, flags)
+
+
+@pytest.mark.parametrize("flags", [1, 3])
+def test_mxfp4_even_special_blocks(flags):
+    g = np.random.default_rng(51)
+    h = 1024
+    allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = allb[((allb >> 7) & 0xFF) != 0xFF]
+    rows = [np.zeros(h, np.uint16), np.full(h, 0x7F7F, np.uint16), g.choice(finite, size=h).astype(np.uint16)]
+    # block maxima right around the even-mode threshold (mantissa 0x5F / 0x60 / 0x7F)
+    for mant in (0x5F, 0x60, 0x7F, 0x00):
+        r = g.integers(0, 0x3F00, size=h).astype(np.uint16)
+        r[::32] = ((g.integers(100, 160, size=h // 32) << 7) | mant).astype(np.uint16)
+        rows.append(r)
+    for s in range(5):
+        f = g.standard_normal(h).astype(np.float32)
+        f[::32] *= 10.0 ** (s * 5 - 12)
+        rows.append(oracle.f32_to_bf16_rne(f))
+    xb = np.stack(rows)
+    n = xb.shape[0]
+    ids = (np.stack([np.arange(3) + t for t in range(n)]) % 5).astype(np.int32)
+    _mxfp4_case(xb, ids, 5, 3, flags)
+
+
+def test_mxfp4_packed_full_size_sampled():
+    """The outlier workload in even + packed mode, checked on sampled rows."""
+    w = workloads.WORKLOADS[2]
+    ids, _, real = workloads.make_routing(w, 2)
+    x, _ = workloads.make_dense(w, 2, DEV, y_rows=1)
+    m = oracle.mask_routing_padding(ids, real)
+    ref = oracle.create_indices(m, w.n_experts)
+    restore = torch.from_numpy(ref["restore_token_order"].view(np.int32)).to(DEV).view(torch.uint32)
+    s, h, k = w.n_slots, w.hidden, w.top_k
+    q, _ = mod.alloc_dispatch_mxfp4(s, h, DEV, packed=True)
+    mod.moe_dispatch_mxfp4(x, k, restore, q, None, flags=mod.MXFP4_EVEN_SCALE | mod.MXFP4_PACKED_ROWS)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(2)
+    pos = np.unique(g.integers(0, ref["n_routed"], size=600))
+    src = ref["token_expert_order"][pos].astype(np.int64) // k
+    xs = u16(x[torch.from_numpy(src).to(DEV)])
+    pq, ps = oracle.mxfp4_quantize(xs, even=True)
+    np.testing.assert_array_equal(q[torch.from_numpy(pos).to(DEV)].cpu().numpy(), np.concatenate([pq, ps], axis=1))
+
+
+def _combine_epi_case(n, k, e, h, scale, with_residual, seed):
+    g = np.random.default_rng(seed)
+    ids = g.integers(-1, e, size=(n, k)).astype(np.int32)
+    ref = oracle.create_indices(ids, e)
+    v = max(ref["n_routed"], 1)
+    yb = oracle.f32_to_bf16_rne((g.standard_normal((v, h)) * np.exp(g.normal(0, 2, (v, h)))).astype(np.float32))
+    rb = oracle.f32_to_bf16_rne((g.standard_normal((n, h)) * 3).astype(np.float32)) if with_residual else None
+    w = g.random((n, k)).astype(np.float32)
+    restore = torch.from_numpy(ref["restore_token_order"].view(np.int32)).to(DEV).view(torch.uint32)
+    out = torch.empty((n, h), dtype=torch.bfloat16, device=DEV)
+    mod.moe_combine_epilogue(bf16_from_bits(yb, DEV), torch.from_numpy(w).to(DEV), restore, k, out, scale,
+                             None if rb is None else bf16_from_bits(rb, DEV))
+    torch.cuda.synchronize()
+    want = oracle.combine_epilogue(yb, w, ref["restore_token_order"], k, scale, rb)
+    np.testing.assert_array_equal(u16(out), want)
+
+
+@pytest.mark.parametrize("scale", [1.0, 2.5, -0.75, 1e-30])
+@pytest.mark.parametrize("with_residual", [False, True])
+@pytest.mark.parametrize("k", [1, 8, 11])
+def test_combine_epilogue(scale, with_residual, k):
+    _combine_epi_case(300, k, 16, 7168 // 7, scale, with_residual, 60 + k)
+
+
+def test_combine_epilogue_matches_combine_at_identity():
+    w = workloads.WORKLOADS[3]
+    ids, wts, real = workloads.make_routing(w, 3)
+    x, y = workloads.make_dense(w, 3, DEV)
+    m = oracle.mask_routing_padding(ids, real)
+    ref = oracle.create_indices(m, w.n_experts)
+    restore = torch.from_numpy(ref["restore_token_order"].view(np.int32)).to(DEV).view(torch.uint32)
+    d_w = torch.from_numpy(wts).to(DEV)
+    a = torch.empty((w.n_rows, w.hidden), dtype=torch.bfloat16, device=DEV)
+    b = torch.empty_like(a)
+    mod.moe_combine(y, d_w, restore, w.top_k, a)
+    mod.moe_combine_epilogue(y, d_w, restore, w.top_k, b, 1.0, None)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    res = x.clone()
+    mod.moe_combine_epilogue(y, d_w, restore, w.top_k, b, 0.5, res)
+    torch.cuda.synchronize()
+    want = oracle.combine_epilogue(u16(y), wts, ref["restore_token_order"], w.top_k, 0.5, u16(res))
+    np.testing.assert_array_equal(u16(b), want)

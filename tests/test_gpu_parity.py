@@ -275,7 +275,7 @@ def test_argument_errors_on_device():
     x = torch.zeros((10, 32), dtype=torch.bfloat16, device=DEV)
     q, s = mod.alloc_dispatch_mxfp4(100, 32, DEV)
     with pytest.raises(mod.MoeError) as e:
-        mod.moe_dispatch_mxfp4(x, 10, idx["restore_token_order"], q, s, flags=1)
+        mod.moe_dispatch_mxfp4(x, 10, idx["restore_token_order"], q, s, flags=4)
     assert e.value.status == 1
 
 
