@@ -107,6 +107,48 @@ def cpu_baseline(w, cfg, ids, wts, x, y, target_s: float = 15.0):
                       f"{dt:.1f} s, NumPy single-threaded on a {os.cpu_count()}-thread host"}
 
 
+def time_extensions(torch, moe, w, x, y, d_ids, d_w, idx, n_routed, reps):
+    """Event-timed runs of the extension entry points on the same workload,
+    outside the step: int64 ids with aligned scale offsets, even-mode and
+    packed MXFP4 dispatch, and the combine epilogue with a residual."""
+    n, k, h, e = w.n_rows, w.top_k, w.hidden, w.n_experts
+    s, v, r = n * k, n_routed, w.real_tokens
+    ids64 = d_ids.to(torch.int64)
+    ix = moe.alloc_indices(s, e, d_ids.device, scales_offset=True)
+    qp, _ = moe.alloc_dispatch_mxfp4(s, h, d_ids.device, packed=True)
+    q, sc = moe.alloc_dispatch_mxfp4(s, h, d_ids.device)
+    out = torch.empty((n, h), dtype=torch.bfloat16, device=d_ids.device)
+    rest = idx["restore_token_order"]
+    cases = {
+        "indices_i64_scales_offset": (lambda: moe.moe_create_indices(
+            ids64, e, ix["token_expert_order"], ix["expert_start_indices"], ix["restore_token_order"],
+            ix["expert_ids"], ix["expert_usage_stats"], ix["workspace"], ix["scales_offset"], 128),
+            s * 8 + 2 * s * 4 + (3 * e + 4) * 4),
+        "dispatch_mxfp4_even": (lambda: moe.moe_dispatch_mxfp4(x, k, rest, q, sc, flags=moe.MXFP4_EVEN_SCALE),
+                                v * 4 + r * h * 2 + v * (h // 2 + h // 32)),
+        "combine_epilogue_residual": (lambda: moe.moe_combine_epilogue(y, d_w, rest, k, out, 2.5, x),
+                                      s * 4 + v * 4 + v * h * 2 + n * h * 2 + n * h * 2),
+    }
+    if h % 512 == 0:
+        cases["dispatch_mxfp4_even_packed"] = (
+            lambda: moe.moe_dispatch_mxfp4(x, k, rest, qp, None, flags=moe.MXFP4_EVEN_SCALE | moe.MXFP4_PACKED_ROWS),
+            v * 4 + r * h * 2 + v * (h // 2 + h // 32))
+    res = {}
+    for name, (fn, nbytes) in cases.items():
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        res[name] = {"ms": round(ms, 4), "bytes": nbytes, "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    del ix, qp, q, sc, out, ids64
+    return res
+
+
 def copy_ceiling(torch, gib: float = 2.0, reps: int = 10) -> float:
     """Read+write GB/s of a plain device-to-device copy (a measured ceiling)."""
     n = int(gib * (1 << 30))
@@ -133,6 +175,10 @@ def main():
     ap.add_argument("--workload", default="large_prefill_stress", choices=sorted(workloads.BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the step as a HIP graph replay (one launch per step from the host)")
+    ap.add_argument("--no-extensions", action="store_true",
+                    help="skip timing the extension entry points after the step")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy before the steps (counter calibration)")
     args = ap.parse_args()
@@ -195,9 +241,33 @@ def main():
     log(f"warmup done, routed slots V={n_routed}")
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(args.steps)]
+    graph = None
+    if args.graph:
+        # stage boundaries are event nodes inside the captured graph
+        graph_ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for c in calls:
+                c()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for c in calls:
+                c()
+        graph.replay()
+        torch.cuda.synchronize()
+        log("captured the step as one graph")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if graph is not None:
+            ev[i][0].record()
+            graph.replay()
+            for j in range(1, len(STAGES) + 1):
+                ev[i][j].record()
+            continue
         for j, c in enumerate(calls):
             ev[i][j].record()
             c()
@@ -206,6 +276,14 @@ def main():
     wall = time.perf_counter() - t0
     stage_ms = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
                 for j, name in enumerate(STAGES)}
+    if graph is not None:  # a replay is one unit: per-stage times come from an eager pass of the same step
+        eager = [torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
+        for j, c in enumerate(calls):
+            eager[j].record()
+            c()
+        eager[len(STAGES)].record()
+        torch.cuda.synchronize()
+        stage_ms = {name: eager[j].elapsed_time(eager[j + 1]) for j, name in enumerate(STAGES)}
     step_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][len(STAGES)]) for i in range(args.steps)]))
     span_ms = ev[0][0].elapsed_time(ev[-1][len(STAGES)]) / args.steps
     log(f"timed {args.steps} steps: {step_ms:.3f} ms/step (events), span {span_ms:.3f}, wall {wall / args.steps * 1e3:.3f}")
@@ -234,6 +312,8 @@ def main():
                 "traffic": read_traffic(kern, w.name), "algorithmic_bytes_per_launch": bts[dom],
                 "avg_launch_ms": round(stage_ms[dom], 4)}
 
+    extensions = None if args.no_extensions else time_extensions(torch, moe, w, x, y, d_ids, d_w, idx, n_routed,
+                                                                 args.steps)
     copy_gbps = None if args.no_copy_ceiling else copy_ceiling(torch)
     cpu = None
     if not args.no_cpu_baseline:
@@ -249,7 +329,8 @@ def main():
                    "step": "mask+create_indices+dispatch_bf16+dispatch_mxfp4+combine"},
         "gbps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "copy_ceiling_gbps": None if copy_gbps is None else round(copy_gbps, 1),
-        "stages": stages, "pipelines": pipelines, "roofline": roofline, "cpu_baseline": cpu,
+        "stages": stages, "pipelines": pipelines, "graph_replay": bool(args.graph),
+        "extensions": extensions, "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 

@@ -64,37 +64,49 @@ __device__ void chunk_histogram(const IdT* __restrict__ ids, int64_t n_slots, in
   }
 }
 
-// Stable scatter of one chunk.  off[b] (LDS) = position of the chunk's first
-// slot of bucket b.  whist is LDS scratch [kIdxWaves][E+1].  Wave w owns the
-// kIdxRounds*64 consecutive slots starting at begin + w*kIdxRounds*64, so the
-// slot order is wave-major, round, lane -- ascending slot index.
-template <typename IdT>
-__device__ void chunk_scatter(const IdT* __restrict__ ids, int64_t n_slots, int64_t begin,
-                              uint32_t n_experts, int nbits, const uint32_t* off, uint32_t* whist,
-                              uint32_t* __restrict__ teo, uint32_t* __restrict__ restore) {
-  const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
-  const int nb = int(n_experts) + 1;
-  uint32_t* my = whist + wave * nb;
-  const int64_t wbegin = begin + int64_t(wave) * kIdxRounds * kWave;
-
+// One wave's slots of a chunk: wave w owns the kIdxRounds*64 consecutive
+// slots starting at begin + w*kIdxRounds*64, so (wave, round, lane) order is
+// ascending slot index.  Keys and peer masks stay in registers between the
+// counting pass and the scatter pass.
+struct WaveTile {
   uint32_t key[kIdxRounds];
   bool valid[kIdxRounds];
   uint64_t peers[kIdxRounds];
+  int64_t wbegin;
+};
+
+// Load the wave's keys and count them per bucket into its own LDS row
+// whist[wave][0..E] (only this wave touches the row; no atomics).
+template <typename IdT>
+__device__ void wave_counts(const IdT* __restrict__ ids, int64_t n_slots, int64_t begin,
+                            uint32_t n_experts, int nbits, uint32_t* whist, WaveTile& tile) {
+  const int lane = __lane_id(), wave = threadIdx.x / kWave;
+  const int nb = int(n_experts) + 1;
+  uint32_t* my = whist + wave * nb;
+  tile.wbegin = begin + int64_t(wave) * kIdxRounds * kWave;
 #pragma unroll
   for (int r = 0; r < kIdxRounds; ++r) {
-    const int64_t i = wbegin + r * kWave + lane;
-    valid[r] = i < n_slots;
-    key[r] = valid[r] ? bucket_of(ids[i], n_experts) : 0u;
+    const int64_t i = tile.wbegin + r * kWave + lane;
+    tile.valid[r] = i < n_slots;
+    tile.key[r] = tile.valid[r] ? bucket_of(ids[i], n_experts) : 0u;
   }
   for (int b = lane; b < nb; b += kWave) my[b] = 0;
-  // pass 1: per-wave bucket counts (only this wave touches its row)
 #pragma unroll
   for (int r = 0; r < kIdxRounds; ++r) {
-    peers[r] = match_peers(key[r], nbits, valid[r]);
-    if (valid[r] && is_leader(peers[r])) my[key[r]] += uint32_t(__popcll(peers[r]));
+    tile.peers[r] = match_peers(tile.key[r], nbits, tile.valid[r]);
+    if (tile.valid[r] && is_leader(tile.peers[r])) my[tile.key[r]] += uint32_t(__popcll(tile.peers[r]));
   }
-  __syncthreads();
-  // exclusive prefix over waves, seeded with the chunk's bucket start
+}
+
+// Stable scatter after wave_counts and a barrier.  off[b] (LDS) = position
+// of the chunk's first slot of bucket b.  Turns whist into per-wave running
+// starts (exclusive prefix over waves seeded with off), then each slot's
+// position is its wave's running start plus its rank among lower peer lanes.
+__device__ void wave_scatter(const WaveTile& tile, uint32_t n_experts, const uint32_t* off,
+                             uint32_t* whist, uint32_t* __restrict__ teo,
+                             uint32_t* __restrict__ restore) {
+  const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
+  const int nb = int(n_experts) + 1;
   for (int b = tid; b < nb; b += kIdxThreads) {
     uint32_t run = off[b];
     for (int w = 0; w < kIdxWaves; ++w) {
@@ -104,16 +116,16 @@ __device__ void chunk_scatter(const IdT* __restrict__ ids, int64_t n_slots, int6
     }
   }
   __syncthreads();
-  // pass 2: position = wave's running start of the bucket + rank among lower lanes
+  uint32_t* my = whist + wave * nb;
   const uint64_t below = lanes_below();
 #pragma unroll
   for (int r = 0; r < kIdxRounds; ++r) {
     uint32_t pos = 0;
-    if (valid[r]) pos = my[key[r]] + uint32_t(__popcll(peers[r] & below));
-    if (valid[r] && is_leader(peers[r])) my[key[r]] += uint32_t(__popcll(peers[r]));
-    if (valid[r]) {
-      const uint32_t i = uint32_t(wbegin + r * kWave + lane);
-      const bool routed = key[r] < n_experts;
+    if (tile.valid[r]) pos = my[tile.key[r]] + uint32_t(__popcll(tile.peers[r] & below));
+    if (tile.valid[r] && is_leader(tile.peers[r])) my[tile.key[r]] += uint32_t(__popcll(tile.peers[r]));
+    if (tile.valid[r]) {
+      const uint32_t i = uint32_t(tile.wbegin + r * kWave + lane);
+      const bool routed = tile.key[r] < n_experts;
       restore[i] = routed ? pos : kSent;
       teo[pos] = routed ? i : kSent;
     }
@@ -247,7 +259,8 @@ __global__ __launch_bounds__(256) void k_index_zero(IndexWorkspace ws, int64_t n
 }
 
 // n_chunks == 1: one workgroup does histogram, scan and scatter.
-// n_chunks > 1: histogram + lookback + (last ticket) CSR outputs.
+// n_chunks > 1: histogram + lookback + (last ticket) CSR outputs; the
+// scatter follows in k_index_scatter.
 template <typename IdT>
 __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
     const IdT* __restrict__ ids, int64_t n_slots, uint32_t n_experts, int nbits,
@@ -260,43 +273,49 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
   const int tid = threadIdx.x;
   uint32_t* hist = lds;
 
-  int64_t c = 0;
-  if (n_chunks > 1) {
-    if (tid == 0) s_chunk = int64_t(atomicAdd(ws.ticket, 1u));
+  if (n_chunks == 1) {
+    // one workgroup: count per wave, total the counts, scan, scatter
+    uint32_t* base = lds + nb;
+    uint32_t* whist = lds + 2 * nb;
+    WaveTile tile;
+    wave_counts(ids, n_slots, 0, n_experts, nbits, whist, tile);
     __syncthreads();
-    c = s_chunk;
+    for (int b = tid; b < nb; b += kIdxThreads) {
+      uint32_t t = 0;
+      for (int w = 0; w < kIdxWaves; ++w) t += whist[w * nb + b];
+      hist[b] = t;
+    }
+    __syncthreads();
+    finalize_counts(hist, n_experts, base, esi, expert_ids, stats, soff, align);
+    __syncthreads();
+    wave_scatter(tile, n_experts, base, whist, teo, restore);
+    return;
   }
+
+  if (tid == 0) s_chunk = int64_t(atomicAdd(ws.ticket, 1u));
   for (int b = tid; b < nb; b += kIdxThreads) hist[b] = 0;
   __syncthreads();
+  const int64_t c = s_chunk;
   chunk_histogram(ids, n_slots, c * kIdxChunk, n_experts, nbits, hist);
   __syncthreads();
 
-  if (n_chunks > 1) {
-    for (int b = tid; b < nb; b += kIdxThreads) {
-      const uint32_t local = hist[b];
-      uint64_t* word = &ws.flags[c * nb + b];
-      uint32_t excl = 0;
-      if (c == 0) {
-        agent_store_u64(word, kFlagPrefix | local);
-      } else {
-        agent_store_u64(word, kFlagAggregate | local);
-        excl = lookback(ws.flags, c, nb, b, ws.err);
-        agent_store_u64(word, kFlagPrefix | (excl + local));
-      }
-      ws.prefix[c * nb + b] = excl;
-      hist[b] = excl + local;
+  for (int b = tid; b < nb; b += kIdxThreads) {
+    const uint32_t local = hist[b];
+    uint64_t* word = &ws.flags[c * nb + b];
+    uint32_t excl = 0;
+    if (c == 0) {
+      agent_store_u64(word, kFlagPrefix | local);
+    } else {
+      agent_store_u64(word, kFlagAggregate | local);
+      excl = lookback(ws.flags, c, nb, b, ws.err);
+      agent_store_u64(word, kFlagPrefix | (excl + local));
     }
-    __syncthreads();
+    ws.prefix[c * nb + b] = excl;
+    hist[b] = excl + local;
   }
+  __syncthreads();
 
-  if (c == n_chunks - 1) {
-    uint32_t* base = n_chunks > 1 ? ws.base : lds + nb;
-    finalize_counts(hist, n_experts, base, esi, expert_ids, stats, soff, align);
-    if (n_chunks == 1) {
-      __syncthreads();
-      chunk_scatter(ids, n_slots, 0, n_experts, nbits, lds + nb, lds + 2 * nb, teo, restore);
-    }
-  }
+  if (c == n_chunks - 1) finalize_counts(hist, n_experts, ws.base, esi, expert_ids, stats, soff, align);
 }
 
 template <typename IdT>
@@ -307,9 +326,11 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scatter(
   const int nb = int(n_experts) + 1;
   const int64_t c = blockIdx.x;
   uint32_t* off = lds;
+  WaveTile tile;
+  wave_counts(ids, n_slots, c * kIdxChunk, n_experts, nbits, lds + nb, tile);
   for (int b = threadIdx.x; b < nb; b += kIdxThreads) off[b] = ws.base[b] + ws.prefix[c * nb + b];
   __syncthreads();
-  chunk_scatter(ids, n_slots, c * kIdxChunk, n_experts, nbits, off, lds + nb, teo, restore);
+  wave_scatter(tile, n_experts, off, lds + nb, teo, restore);
 }
 
 int64_t index_chunks(int64_t n_slots) {
