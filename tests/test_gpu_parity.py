@@ -157,6 +157,7 @@ CASES = {
     "h8_bf16_only": (15, 64, 2, 4, 8, "uniform"),
     "h_large": (16, 20, 2, 4, 16384, "uniform"),
     "h_ragged_vectors": (17, 30, 3, 6, 32 * 37, "uniform"),
+    "k1024_e1024": (18, 6, 1024, 1024, 32, "distinct"),
 }
 
 
@@ -329,3 +330,65 @@ def test_graph_replay_with_device_count():
         np.testing.assert_array_equal(q[:v].cpu().numpy(), wq)
         np.testing.assert_array_equal(sc[:v].cpu().numpy(), wsc)
         _check_combine(u16(comb), oracle.combine(u16(y), w, ref["restore_token_order"], k))
+
+
+def test_indices_beyond_int32_slots():
+    """2^31 + 4099 slots (past the int32 range, ragged last chunk), E = 1024:
+    every property that defines the outputs, checked on the GPU in pieces."""
+    S, E = (1 << 31) + 4099, 1024
+    print(f"[parity] create_indices at S={S} E={E}", flush=True)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(20261203)
+    ids = torch.randint(-2, E + 6, (S,), generator=gen, device=DEV, dtype=torch.int32)
+    idx = mod.alloc_indices(S, E, DEV)
+    mod.moe_create_indices(ids, E, idx["token_expert_order"], idx["expert_start_indices"],
+                           idx["restore_token_order"], idx["expert_ids"], idx["expert_usage_stats"],
+                           idx["workspace"])
+    torch.cuda.synchronize()
+    assert int(idx["workspace"][:4].view(torch.int32).item()) == 0
+
+    def as_i64(t):
+        return t.view(torch.int32).to(torch.int64) & 0xFFFFFFFF
+
+    routed = (ids >= 0) & (ids < E)
+    counts = torch.zeros(E, dtype=torch.int64, device=DEV)
+    step = 1 << 28
+    for a in range(0, S, step):
+        sl = ids[a:a + step]
+        r = routed[a:a + step]
+        counts += torch.bincount(sl[r].to(torch.int64), minlength=E)
+    v = int(counts.sum().item())
+    active = torch.nonzero(counts > 0).flatten()
+    na = active.numel()
+    esi = as_i64(idx["expert_start_indices"])
+    assert int(esi[0]) == 0 and int(esi[na]) == v and bool((esi[na:] == v).all())
+    assert torch.equal(esi[1:na + 1] - esi[:na], counts[active])
+    assert torch.equal(idx["expert_ids"][:na].to(torch.int64), active)
+    assert bool((idx["expert_ids"][na:] == -1).all())
+    st = as_i64(idx["expert_usage_stats"])
+    assert int(st[0]) == int(counts.max()) and int(st[1]) == na
+    teo, res = idx["token_expert_order"], idx["restore_token_order"]
+    prev_key = prev_slot = None
+    for a in range(0, v, step):
+        b = min(v, a + step)
+        t = as_i64(teo[a:b])
+        assert bool((t < S).all())
+        k = ids[t].to(torch.int64)
+        assert bool(((k >= 0) & (k < E)).all())
+        if prev_key is not None:
+            k = torch.cat([prev_key, k])
+            t = torch.cat([prev_slot, t])
+        dk = k[1:] - k[:-1]
+        assert bool((dk >= 0).all())
+        assert bool(((t[1:] - t[:-1]) > 0)[dk == 0].all())  # stable within an expert
+        prev_key, prev_slot = k[-1:], t[-1:]
+        pos = as_i64(res.view(torch.int32)[as_i64(teo[a:b])])
+        assert torch.equal(pos, torch.arange(a, b, device=DEV))
+    assert bool((as_i64(teo[v:]) == 0xFFFFFFFF).all())
+    n_unrouted = 0
+    for a in range(0, S, step):
+        r = routed[a:a + step]
+        rr = as_i64(res[a:a + step])
+        assert bool((rr[~r] == 0xFFFFFFFF).all()) and bool((rr[r] < v).all())
+        n_unrouted += int((~r).sum())
+    assert n_unrouted == S - v
