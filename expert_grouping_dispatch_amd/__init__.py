@@ -128,7 +128,7 @@ def moe_create_indices_workspace_bytes(n_slots: int, n_experts: int) -> int:
 
 
 def alloc_indices(n_slots: int, n_experts: int, device, scales_offset: bool = False) -> dict:
-    """Empty output tensors and workspace for moe_create_indices."""
+    """Output tensors (uninitialised) and a zero-filled workspace for moe_create_indices."""
     device = torch.device(device)
     ws = moe_create_indices_workspace_bytes(n_slots, n_experts)
     if ws == 0:
@@ -140,7 +140,7 @@ def alloc_indices(n_slots: int, n_experts: int, device, scales_offset: bool = Fa
         restore_token_order=torch.empty(n_slots, **u32),
         expert_ids=torch.empty(n_experts, dtype=torch.int32, device=device),
         expert_usage_stats=torch.empty(2, **u32),
-        workspace=torch.empty(ws, dtype=torch.uint8, device=device),
+        workspace=torch.zeros(ws, dtype=torch.uint8, device=device),  # zero-filled once, reusable
         scales_offset=torch.empty(n_experts + 1, **u32) if scales_offset else None,
     )
 

@@ -4,14 +4,16 @@
 // The pages' kernel is one CTA.  Here the slots are cut into chunks of
 // kIdxChunk; for S <= kIdxChunk one workgroup still does all three steps in
 // one launch, otherwise:
-//   k_index_zero     clears the lookback words and the chunk ticket;
-//   k_index_hist     per chunk: LDS histogram (wave-aggregated increments),
-//                    then a decoupled lookback over earlier chunks gives, per
+//   k_index_hist     per chunk (taken by ticket): LDS histogram, then a
+//                    decoupled lookback over earlier chunks gives, per
 //                    bucket, the number of slots in all earlier chunks; the
 //                    chunk holding the last ticket also has the totals and
 //                    writes the CSR / active-expert / stats outputs;
 //   k_index_scatter  per chunk: stable ranks (wave ballots + per-wave LDS
 //                    counters) -> token_expert_order and restore_token_order.
+// Lookback words carry a per-call tag (the workspace epoch, advanced by the
+// last ticket holder together with the ticket reset), so words left by an
+// earlier call are never taken as published and no clearing pass is needed.
 // Bucket b < E is expert b; bucket E collects the unrouted slots, which land
 // after every routed slot and fill token_expert_order[V, S) with sentinels.
 #include "common.h"
@@ -21,9 +23,11 @@ namespace moe {
 
 namespace {
 
+// lookback word: [63:34] call tag, [33:32] status, [31:0] count
 constexpr uint64_t kFlagAggregate = uint64_t(1) << 32;  // count of this chunk only
 constexpr uint64_t kFlagPrefix = uint64_t(2) << 32;     // count of chunks [0, c]
-constexpr uint64_t kFlagStatusMask = ~uint64_t(0xFFFFFFFFu);
+constexpr int kTagShift = 34;
+constexpr uint32_t kTagMask = 0x3FFFFFFFu;
 constexpr uint32_t kSpinLimit = 1u << 20;
 #ifndef MOE_LOOKBACK_WINDOW
 #define MOE_LOOKBACK_WINDOW 8
@@ -45,9 +49,10 @@ __device__ __forceinline__ bool is_leader(uint64_t peers) {
 }
 
 // Count the chunk's slots per bucket into hist[0..E] (LDS, zeroed by caller).
+// Only totals are needed here, so plain LDS atomics do.
 template <typename IdT>
 __device__ void chunk_histogram(const IdT* __restrict__ ids, int64_t n_slots, int64_t begin,
-                                uint32_t n_experts, int nbits, uint32_t* hist) {
+                                uint32_t n_experts, uint32_t* hist) {
   const int tid = threadIdx.x;
   uint32_t key[kIdxRounds];
   bool valid[kIdxRounds];
@@ -58,10 +63,8 @@ __device__ void chunk_histogram(const IdT* __restrict__ ids, int64_t n_slots, in
     key[r] = valid[r] ? bucket_of(ids[i], n_experts) : 0u;
   }
 #pragma unroll
-  for (int r = 0; r < kIdxRounds; ++r) {
-    const uint64_t peers = match_peers(key[r], nbits, valid[r]);
-    if (valid[r] && is_leader(peers)) atomicAdd(&hist[key[r]], uint32_t(__popcll(peers)));
-  }
+  for (int r = 0; r < kIdxRounds; ++r)
+    if (valid[r]) atomicAdd(&hist[key[r]], 1u);
 }
 
 // One wave's slots of a chunk: wave w owns the kIdxRounds*64 consecutive
@@ -214,11 +217,13 @@ __device__ void finalize_counts(const uint32_t* tot, uint32_t n_experts, uint32_
 
 // Number of slots of bucket b in chunks [0, c): walk back over earlier chunks'
 // words, kLookbackWindow at a time, adding per-chunk counts until a chunk
-// that already published its inclusive prefix.  Every earlier chunk is held
-// by a workgroup that took its ticket first and publishes its own count
-// without waiting, so the wait ends; kSpinLimit is a backstop that records
-// an error instead of spinning forever.
-__device__ uint32_t lookback(const uint64_t* flags, int64_t c, int nb, int b, uint32_t* err) {
+// that already published its inclusive prefix.  Only words with this call's
+// tag count as published.  Every earlier chunk is held by a workgroup that
+// took its ticket first and publishes its own count without waiting, so the
+// wait ends; kSpinLimit is a backstop that records an error instead of
+// spinning forever.
+__device__ uint32_t lookback(const uint64_t* flags, int64_t c, int nb, int b, uint32_t tag,
+                             uint32_t* err) {
   uint32_t excl = 0;
   int64_t cc = c - 1;
   uint32_t spins = 0;
@@ -226,17 +231,18 @@ __device__ uint32_t lookback(const uint64_t* flags, int64_t c, int nb, int b, ui
     uint64_t f[kLookbackWindow];
 #pragma unroll
     for (int w = 0; w < kLookbackWindow; ++w)
-      f[w] = (cc - w >= 0) ? agent_load_u64(&flags[(cc - w) * nb + b]) : kFlagPrefix;
+      f[w] = (cc - w >= 0) ? agent_load_u64(&flags[(cc - w) * nb + b])
+                           : ((uint64_t(tag) << kTagShift) | kFlagPrefix);
     int used = 0;
     bool done = false;
 #pragma unroll
     for (int w = 0; w < kLookbackWindow; ++w) {
       if (done || used < w) continue;
-      const uint64_t st = f[w] & kFlagStatusMask;
-      if (st == 0) continue;  // not yet published: poll again from here
+      const uint32_t st = uint32_t(f[w] >> 32) & 3u;
+      if (uint32_t(f[w] >> kTagShift) != tag || st == 0) continue;  // not yet published
       excl += uint32_t(f[w]);
       used = w + 1;
-      if (st == kFlagPrefix) done = true;
+      if (st == 2u) done = true;
     }
     if (done) return excl;
     cc -= used;
@@ -249,15 +255,6 @@ __device__ uint32_t lookback(const uint64_t* flags, int64_t c, int nb, int b, ui
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void k_index_zero(IndexWorkspace ws, int64_t n_flags) {
-  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n_flags) ws.flags[i] = 0;
-  if (i == 0) {
-    *ws.ticket = 0;
-    *ws.err = 0;
-  }
-}
-
 // n_chunks == 1: one workgroup does histogram, scan and scatter.
 // n_chunks > 1: histogram + lookback + (last ticket) CSR outputs; the
 // scatter follows in k_index_scatter.
@@ -269,6 +266,7 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
     uint32_t align, uint32_t* __restrict__ teo, uint32_t* __restrict__ restore) {
   extern __shared__ uint32_t lds[];
   __shared__ int64_t s_chunk;
+  __shared__ uint32_t s_epoch;
   const int nb = int(n_experts) + 1;
   const int tid = threadIdx.x;
   uint32_t* hist = lds;
@@ -292,11 +290,19 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
     return;
   }
 
-  if (tid == 0) s_chunk = int64_t(atomicAdd(ws.ticket, 1u));
+  if (tid == 0) {
+    // the epoch read completes before this workgroup publishes anything, and
+    // the last ticket holder advances it only after every chunk has published
+    s_epoch = __hip_atomic_load(ws.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_chunk = int64_t(__hip_atomic_fetch_add(ws.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  }
   for (int b = tid; b < nb; b += kIdxThreads) hist[b] = 0;
   __syncthreads();
   const int64_t c = s_chunk;
-  chunk_histogram(ids, n_slots, c * kIdxChunk, n_experts, nbits, hist);
+  const uint32_t epoch = s_epoch;
+  const uint32_t tag = epoch & kTagMask;
+  const uint64_t tagbits = uint64_t(tag) << kTagShift;
+  chunk_histogram(ids, n_slots, c * kIdxChunk, n_experts, hist);
   __syncthreads();
 
   for (int b = tid; b < nb; b += kIdxThreads) {
@@ -304,18 +310,24 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
     uint64_t* word = &ws.flags[c * nb + b];
     uint32_t excl = 0;
     if (c == 0) {
-      agent_store_u64(word, kFlagPrefix | local);
+      agent_store_u64(word, tagbits | kFlagPrefix | local);
     } else {
-      agent_store_u64(word, kFlagAggregate | local);
-      excl = lookback(ws.flags, c, nb, b, ws.err);
-      agent_store_u64(word, kFlagPrefix | (excl + local));
+      agent_store_u64(word, tagbits | kFlagAggregate | local);
+      excl = lookback(ws.flags, c, nb, b, tag, ws.err);
+      agent_store_u64(word, tagbits | kFlagPrefix | (excl + local));
     }
     ws.prefix[c * nb + b] = excl;
     hist[b] = excl + local;
   }
   __syncthreads();
 
-  if (c == n_chunks - 1) finalize_counts(hist, n_experts, ws.base, esi, expert_ids, stats, soff, align);
+  if (c == n_chunks - 1) {
+    finalize_counts(hist, n_experts, ws.base, esi, expert_ids, stats, soff, align);
+    if (tid == 0) {  // every ticket of this call is taken: reset for the next call
+      __hip_atomic_store(ws.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ws.epoch, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 template <typename IdT>
@@ -326,9 +338,21 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scatter(
   const int nb = int(n_experts) + 1;
   const int64_t c = blockIdx.x;
   uint32_t* off = lds;
+  // start the offset loads before the key work so both are in flight together
+  constexpr int kMaxPerThread = (MOE_MAX_BUCKETS + kIdxThreads - 1) / kIdxThreads;
+  uint32_t offv[kMaxPerThread];
+#pragma unroll
+  for (int q = 0; q < kMaxPerThread; ++q) {
+    const int b = threadIdx.x + q * kIdxThreads;
+    offv[q] = b < nb ? ws.base[b] + ws.prefix[c * nb + b] : 0u;
+  }
   WaveTile tile;
   wave_counts(ids, n_slots, c * kIdxChunk, n_experts, nbits, lds + nb, tile);
-  for (int b = threadIdx.x; b < nb; b += kIdxThreads) off[b] = ws.base[b] + ws.prefix[c * nb + b];
+#pragma unroll
+  for (int q = 0; q < kMaxPerThread; ++q) {
+    const int b = threadIdx.x + q * kIdxThreads;
+    if (b < nb) off[b] = offv[q];
+  }
   __syncthreads();
   wave_scatter(tile, n_experts, off, lds + nb, teo, restore);
 }
@@ -348,6 +372,7 @@ IndexWorkspace index_workspace_carve(void* ws, int64_t n_slots, int n_experts) {
   IndexWorkspace w;
   w.err = reinterpret_cast<uint32_t*>(p);
   w.ticket = reinterpret_cast<uint32_t*>(p + 4);
+  w.epoch = reinterpret_cast<uint32_t*>(p + 8);
   p += 256;
   w.flags = reinterpret_cast<uint64_t*>(p);
   p += align256(c * nb * 8);
@@ -373,15 +398,10 @@ hipError_t launch_create_indices(const IdT* ids, int64_t n_slots, int n_experts,
                        teo, restore);
     return hipGetLastError();
   }
-  const int64_t n_flags = chunks * nb;
-  hipLaunchKernelGGL(k_index_zero, dim3(uint32_t((n_flags + 255) / 256)), dim3(256), 0, s, ws,
-                     n_flags);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_index_hist<IdT>, dim3(uint32_t(chunks)), dim3(kIdxThreads),
                      size_t(nb) * sizeof(uint32_t), s, ids, n_slots, uint32_t(n_experts), nbits,
                      chunks, ws, esi, expert_ids, stats, soff, align, teo, restore);
-  e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_index_scatter<IdT>, dim3(uint32_t(chunks)), dim3(kIdxThreads),
                      size_t(1 + kIdxWaves) * nb * sizeof(uint32_t), s, ids, n_slots,

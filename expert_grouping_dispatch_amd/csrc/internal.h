@@ -21,10 +21,15 @@ constexpr int kIdxThreads = MOE_IDX_THREADS;
 constexpr int kIdxWaves = kIdxThreads / 64;
 constexpr int kIdxRounds = MOE_IDX_ROUNDS;
 constexpr int64_t kIdxChunk = int64_t(kIdxThreads) * kIdxRounds;
+#define MOE_MAX_BUCKETS 1025  // experts + the unrouted bucket
 
+// Header words start at zero (the caller zero-fills the workspace once) and
+// are kept consistent by the kernels: the ticket is reset and the epoch
+// advanced at the end of every multi-chunk call.
 struct IndexWorkspace {
-  uint32_t* err;        // [1]  nonzero if a cross-workgroup wait gave up
+  uint32_t* err;        // [1]  nonzero once a cross-workgroup wait gave up (sticky)
   uint32_t* ticket;     // [1]  chunk ticket counter
+  uint32_t* epoch;      // [1]  call counter; tags the lookback words
   uint64_t* flags;      // [chunks][E+1] (status << 32 | count) lookback words
   uint32_t* prefix;     // [chunks][E+1] slots of bucket b in chunks before c
   uint32_t* base;       // [E+1]         first position of bucket b

@@ -129,8 +129,13 @@ size_t moe_create_indices_workspace_bytes(int64_t n_slots, int32_t n_experts);
  *                         S + E*scales_align must stay below 2^32.
  *   workspace             [device] scratch of at least
  *                         moe_create_indices_workspace_bytes(S, E) bytes,
- *                         256-byte aligned, no initial contents required.
+ *                         256-byte aligned, zero-filled once before its first
+ *                         use; every call leaves it ready for the next one
+ *                         (any S and E up to the size it was made for).
  *                         Calls that share a workspace must not overlap.
+ *                         Its first 32-bit word becomes nonzero (and stays
+ *                         so) if a cross-workgroup wait ever gave up, which
+ *                         a non-zeroed workspace can cause.
  * All outputs are fully written, also when S = 0 or V = 0.
  */
 int moe_create_indices(const int32_t* topk_ids, int64_t n_slots, int32_t n_experts,

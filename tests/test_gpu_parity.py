@@ -392,3 +392,21 @@ def test_indices_beyond_int32_slots():
         assert bool((rr[~r] == 0xFFFFFFFF).all()) and bool((rr[r] < v).all())
         n_unrouted += int((~r).sum())
     assert n_unrouted == S - v
+
+
+def test_workspace_reuse_across_shapes():
+    """One zero-filled workspace serves calls of different sizes and expert
+    counts in any order (lookback words of earlier calls never count)."""
+    shapes = [(40000, 8, 256), (10000, 8, 64), (40000, 8, 256), (300, 4, 16), (70000, 8, 1024),
+              (9000, 8, 256), (40000, 8, 256)]
+    ws_bytes = max(mod.moe_create_indices_workspace_bytes(n * k, e) for n, k, e in shapes)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=DEV)
+    for i, (n, k, e) in enumerate(shapes):
+        ids, _, _, _, _ = _rand_case(900 + i, n, k, e, 8, "distinct" if k <= e else "uniform")
+        d_ids = torch.from_numpy(ids).to(DEV)
+        idx = mod.alloc_indices(n * k, e, DEV)
+        mod.moe_create_indices(d_ids, e, idx["token_expert_order"], idx["expert_start_indices"],
+                               idx["restore_token_order"], idx["expert_ids"], idx["expert_usage_stats"], ws)
+        torch.cuda.synchronize()
+        check_indices(idx, oracle.create_indices(ids, e))
+    assert int(ws[:4].view(torch.int32).item()) == 0
