@@ -55,6 +55,26 @@ def _compile(src: str) -> str:
     return obj
 
 
+C_EXAMPLE_SRC = os.path.join(ROOT, "tests", "c_abi", "route_smoke.c")
+C_EXAMPLE_BIN = os.path.join(ROOT, "tests", "c_abi", "route_smoke.bin")
+
+
+def build_c_example(verbose: bool = True) -> str:
+    """A plain-C program (no torch) linked against the library: it shows the
+    C ABI is usable on its own; a GPU test runs it."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = ["gcc", "-O2", "-std=c11", "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE, "-I", os.path.join(rocm, "include"),
+           C_EXAMPLE_SRC, "-o", C_EXAMPLE_BIN, "-L", PKG, "-lmoe_route",
+           "-Wl,-rpath,$ORIGIN/../../expert_grouping_dispatch_amd",
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64", f"-Wl,-rpath,{os.path.join(rocm, 'lib')}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"C example build failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {C_EXAMPLE_BIN}", flush=True)
+    return C_EXAMPLE_BIN
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
@@ -68,6 +88,7 @@ def build(verbose: bool = True) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources", flush=True)
+    build_c_example(verbose)
     return LIB
 
 
