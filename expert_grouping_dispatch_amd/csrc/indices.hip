@@ -11,9 +11,10 @@
 //                    writes the CSR / active-expert / stats outputs;
 //   k_index_scatter  per chunk: stable ranks (wave ballots + per-wave LDS
 //                    counters) -> token_expert_order and restore_token_order.
-// Lookback words carry a per-call tag (the workspace epoch, advanced by the
-// last ticket holder together with the ticket reset), so words left by an
-// earlier call are never taken as published and no clearing pass is needed.
+// The workspace layout does not depend on the call's shape (header, bucket
+// starts, then the lookback words), and k_index_scatter zeroes every lookback
+// word it has read, so between calls the word region holds zeros only and a
+// later call of any shape finds no published word it did not write.
 // Bucket b < E is expert b; bucket E collects the unrouted slots, which land
 // after every routed slot and fill token_expert_order[V, S) with sentinels.
 #include "common.h"
@@ -23,11 +24,9 @@ namespace moe {
 
 namespace {
 
-// lookback word: [63:34] call tag, [33:32] status, [31:0] count
+// lookback word: [33:32] status (0 = not yet published), [31:0] count
 constexpr uint64_t kFlagAggregate = uint64_t(1) << 32;  // count of this chunk only
 constexpr uint64_t kFlagPrefix = uint64_t(2) << 32;     // count of chunks [0, c]
-constexpr int kTagShift = 34;
-constexpr uint32_t kTagMask = 0x3FFFFFFFu;
 constexpr uint32_t kSpinLimit = 1u << 20;
 #ifndef MOE_LOOKBACK_WINDOW
 #define MOE_LOOKBACK_WINDOW 8
@@ -102,9 +101,11 @@ __device__ void wave_counts(const IdT* __restrict__ ids, int64_t n_slots, int64_
 }
 
 // Stable scatter after wave_counts and a barrier.  off[b] (LDS) = position
-// of the chunk's first slot of bucket b.  Turns whist into per-wave running
-// starts (exclusive prefix over waves seeded with off), then each slot's
-// position is its wave's running start plus its rank among lower peer lanes.
+// of the chunk's first slot of bucket b, or with kFromEnd the position just
+// past its last one.  Turns whist into per-wave running starts (exclusive
+// prefix over waves seeded with the chunk's start), then each slot's position
+// is its wave's running start plus its rank among lower peer lanes.
+template <bool kFromEnd>
 __device__ void wave_scatter(const WaveTile& tile, uint32_t n_experts, const uint32_t* off,
                              uint32_t* whist, uint32_t* __restrict__ teo,
                              uint32_t* __restrict__ restore) {
@@ -112,6 +113,8 @@ __device__ void wave_scatter(const WaveTile& tile, uint32_t n_experts, const uin
   const int nb = int(n_experts) + 1;
   for (int b = tid; b < nb; b += kIdxThreads) {
     uint32_t run = off[b];
+    if (kFromEnd)
+      for (int w = 0; w < kIdxWaves; ++w) run -= whist[w * nb + b];
     for (int w = 0; w < kIdxWaves; ++w) {
       const uint32_t c = whist[w * nb + b];
       whist[w * nb + b] = run;
@@ -217,13 +220,11 @@ __device__ void finalize_counts(const uint32_t* tot, uint32_t n_experts, uint32_
 
 // Number of slots of bucket b in chunks [0, c): walk back over earlier chunks'
 // words, kLookbackWindow at a time, adding per-chunk counts until a chunk
-// that already published its inclusive prefix.  Only words with this call's
-// tag count as published.  Every earlier chunk is held by a workgroup that
-// took its ticket first and publishes its own count without waiting, so the
-// wait ends; kSpinLimit is a backstop that records an error instead of
-// spinning forever.
-__device__ uint32_t lookback(const uint64_t* flags, int64_t c, int nb, int b, uint32_t tag,
-                             uint32_t* err) {
+// that already published its inclusive prefix.  Every earlier chunk is held
+// by a workgroup that took its ticket first and publishes its own count
+// without waiting, so the wait ends; kSpinLimit is a backstop that records an
+// error instead of spinning forever.
+__device__ uint32_t lookback(const uint64_t* flags, int64_t c, int nb, int b, uint32_t* err) {
   uint32_t excl = 0;
   int64_t cc = c - 1;
   uint32_t spins = 0;
@@ -231,15 +232,14 @@ __device__ uint32_t lookback(const uint64_t* flags, int64_t c, int nb, int b, ui
     uint64_t f[kLookbackWindow];
 #pragma unroll
     for (int w = 0; w < kLookbackWindow; ++w)
-      f[w] = (cc - w >= 0) ? agent_load_u64(&flags[(cc - w) * nb + b])
-                           : ((uint64_t(tag) << kTagShift) | kFlagPrefix);
+      f[w] = (cc - w >= 0) ? agent_load_u64(&flags[(cc - w) * nb + b]) : kFlagPrefix;
     int used = 0;
     bool done = false;
 #pragma unroll
     for (int w = 0; w < kLookbackWindow; ++w) {
       if (done || used < w) continue;
       const uint32_t st = uint32_t(f[w] >> 32) & 3u;
-      if (uint32_t(f[w] >> kTagShift) != tag || st == 0) continue;  // not yet published
+      if (st == 0) continue;  // not yet published
       excl += uint32_t(f[w]);
       used = w + 1;
       if (st == 2u) done = true;
@@ -266,7 +266,6 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
     uint32_t align, uint32_t* __restrict__ teo, uint32_t* __restrict__ restore) {
   extern __shared__ uint32_t lds[];
   __shared__ int64_t s_chunk;
-  __shared__ uint32_t s_epoch;
   const int nb = int(n_experts) + 1;
   const int tid = threadIdx.x;
   uint32_t* hist = lds;
@@ -286,22 +285,16 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
     __syncthreads();
     finalize_counts(hist, n_experts, base, esi, expert_ids, stats, soff, align);
     __syncthreads();
-    wave_scatter(tile, n_experts, base, whist, teo, restore);
+    wave_scatter<false>(tile, n_experts, base, whist, teo, restore);
     return;
   }
 
   if (tid == 0) {
-    // the epoch read completes before this workgroup publishes anything, and
-    // the last ticket holder advances it only after every chunk has published
-    s_epoch = __hip_atomic_load(ws.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_chunk = int64_t(__hip_atomic_fetch_add(ws.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   }
   for (int b = tid; b < nb; b += kIdxThreads) hist[b] = 0;
   __syncthreads();
   const int64_t c = s_chunk;
-  const uint32_t epoch = s_epoch;
-  const uint32_t tag = epoch & kTagMask;
-  const uint64_t tagbits = uint64_t(tag) << kTagShift;
   chunk_histogram(ids, n_slots, c * kIdxChunk, n_experts, hist);
   __syncthreads();
 
@@ -310,23 +303,20 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
     uint64_t* word = &ws.flags[c * nb + b];
     uint32_t excl = 0;
     if (c == 0) {
-      agent_store_u64(word, tagbits | kFlagPrefix | local);
+      agent_store_u64(word, kFlagPrefix | local);
     } else {
-      agent_store_u64(word, tagbits | kFlagAggregate | local);
-      excl = lookback(ws.flags, c, nb, b, tag, ws.err);
-      agent_store_u64(word, tagbits | kFlagPrefix | (excl + local));
+      agent_store_u64(word, kFlagAggregate | local);
+      excl = lookback(ws.flags, c, nb, b, ws.err);
+      agent_store_u64(word, kFlagPrefix | (excl + local));
     }
-    ws.prefix[c * nb + b] = excl;
     hist[b] = excl + local;
   }
   __syncthreads();
 
   if (c == n_chunks - 1) {
     finalize_counts(hist, n_experts, ws.base, esi, expert_ids, stats, soff, align);
-    if (tid == 0) {  // every ticket of this call is taken: reset for the next call
+    if (tid == 0)  // every ticket of this call is taken: reset for the next call
       __hip_atomic_store(ws.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(ws.epoch, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
   }
 }
 
@@ -338,13 +328,22 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scatter(
   const int nb = int(n_experts) + 1;
   const int64_t c = blockIdx.x;
   uint32_t* off = lds;
-  // start the offset loads before the key work so both are in flight together
+  // Start the offset loads before the key work so both are in flight
+  // together.  The chunk's word holds the slots of bucket b in chunks [0, c];
+  // base + that count is the end of the chunk's run of bucket b.  The word is
+  // then zeroed for the next call (the previous kernel wrote it; nothing else
+  // reads it).
   constexpr int kMaxPerThread = (MOE_MAX_BUCKETS + kIdxThreads - 1) / kIdxThreads;
   uint32_t offv[kMaxPerThread];
 #pragma unroll
   for (int q = 0; q < kMaxPerThread; ++q) {
     const int b = threadIdx.x + q * kIdxThreads;
-    offv[q] = b < nb ? ws.base[b] + ws.prefix[c * nb + b] : 0u;
+    offv[q] = b < nb ? ws.base[b] + uint32_t(ws.flags[c * nb + b]) : 0u;
+  }
+#pragma unroll
+  for (int q = 0; q < kMaxPerThread; ++q) {
+    const int b = threadIdx.x + q * kIdxThreads;
+    if (b < nb) ws.flags[c * nb + b] = 0u;
   }
   WaveTile tile;
   wave_counts(ids, n_slots, c * kIdxChunk, n_experts, nbits, lds + nb, tile);
@@ -354,31 +353,33 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scatter(
     if (b < nb) off[b] = offv[q];
   }
   __syncthreads();
-  wave_scatter(tile, n_experts, off, lds + nb, teo, restore);
+  wave_scatter<true>(tile, n_experts, off, lds + nb, teo, restore);
 }
 
 int64_t index_chunks(int64_t n_slots) {
   return n_slots <= kIdxChunk ? 1 : (n_slots + kIdxChunk - 1) / kIdxChunk;
 }
 
+// Fixed layout for every shape: header words, bucket starts for the largest
+// expert count, then the lookback words [chunks][E+1] of this call.
+constexpr size_t kWsHeader = 256;
+constexpr size_t kWsBase = kWsHeader;
+constexpr size_t kWsFlags = kWsBase + ((size_t(MOE_MAX_BUCKETS) * 4 + 255) & ~size_t(255));
+
 size_t index_workspace_bytes(int64_t n_slots, int n_experts) {
   const size_t c = size_t(index_chunks(n_slots)), nb = size_t(n_experts) + 1;
-  return 256 + align256(c * nb * 8) + align256(c * nb * 4) + align256(nb * 4);
+  return kWsFlags + align256(c * nb * 8);
 }
 
 IndexWorkspace index_workspace_carve(void* ws, int64_t n_slots, int n_experts) {
-  const size_t c = size_t(index_chunks(n_slots)), nb = size_t(n_experts) + 1;
+  (void)n_slots;
+  (void)n_experts;
   char* p = static_cast<char*>(ws);
   IndexWorkspace w;
   w.err = reinterpret_cast<uint32_t*>(p);
   w.ticket = reinterpret_cast<uint32_t*>(p + 4);
-  w.epoch = reinterpret_cast<uint32_t*>(p + 8);
-  p += 256;
-  w.flags = reinterpret_cast<uint64_t*>(p);
-  p += align256(c * nb * 8);
-  w.prefix = reinterpret_cast<uint32_t*>(p);
-  p += align256(c * nb * 4);
-  w.base = reinterpret_cast<uint32_t*>(p);
+  w.base = reinterpret_cast<uint32_t*>(p + kWsBase);
+  w.flags = reinterpret_cast<uint64_t*>(p + kWsFlags);
   return w;
 }
 

@@ -23,16 +23,14 @@ constexpr int kIdxRounds = MOE_IDX_ROUNDS;
 constexpr int64_t kIdxChunk = int64_t(kIdxThreads) * kIdxRounds;
 #define MOE_MAX_BUCKETS 1025  // experts + the unrouted bucket
 
-// Header words start at zero (the caller zero-fills the workspace once) and
-// are kept consistent by the kernels: the ticket is reset and the epoch
-// advanced at the end of every multi-chunk call.
+// The caller zero-fills the workspace once.  The kernels keep it ready for
+// the next call of any shape: the last ticket holder resets the ticket, and
+// the scatter kernel zeroes every lookback word of the call after reading it.
 struct IndexWorkspace {
   uint32_t* err;        // [1]  nonzero once a cross-workgroup wait gave up (sticky)
   uint32_t* ticket;     // [1]  chunk ticket counter
-  uint32_t* epoch;      // [1]  call counter; tags the lookback words
-  uint64_t* flags;      // [chunks][E+1] (status << 32 | count) lookback words
-  uint32_t* prefix;     // [chunks][E+1] slots of bucket b in chunks before c
   uint32_t* base;       // [E+1]         first position of bucket b
+  uint64_t* flags;      // [chunks][E+1] (status << 32 | count) lookback words
 };
 
 int64_t index_chunks(int64_t n_slots);

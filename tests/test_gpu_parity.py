@@ -395,18 +395,25 @@ def test_indices_beyond_int32_slots():
 
 
 def test_workspace_reuse_across_shapes():
-    """One zero-filled workspace serves calls of different sizes and expert
-    counts in any order (lookback words of earlier calls never count)."""
+    """One zero-filled workspace serves calls of different sizes, expert
+    counts and id widths in any order: nothing an earlier call left in it is
+    taken as this call's (small calls first, then a larger footprint)."""
     shapes = [(40000, 8, 256), (10000, 8, 64), (40000, 8, 256), (300, 4, 16), (70000, 8, 1024),
-              (9000, 8, 256), (40000, 8, 256)]
+              (9000, 8, 256), (40000, 8, 256), (513, 8, 8), (70000, 8, 1024), (20000, 8, 1000),
+              (60000, 8, 3), (4097, 1, 1024), (70000, 8, 1024)]
+    g = np.random.default_rng(77)
+    shapes += [shapes[j] for j in g.permutation(len(shapes))]
     ws_bytes = max(mod.moe_create_indices_workspace_bytes(n * k, e) for n, k, e in shapes)
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=DEV)
     for i, (n, k, e) in enumerate(shapes):
-        ids, _, _, _, _ = _rand_case(900 + i, n, k, e, 8, "distinct" if k <= e else "uniform")
+        kind = "distinct" if k <= e and n * e <= 10 ** 7 else "uniform"
+        ids, _, _, _, _ = _rand_case(900 + i, n, k, e, 8, kind)
         d_ids = torch.from_numpy(ids).to(DEV)
+        if i % 3 == 2:
+            d_ids = d_ids.to(torch.int64)
         idx = mod.alloc_indices(n * k, e, DEV)
         mod.moe_create_indices(d_ids, e, idx["token_expert_order"], idx["expert_start_indices"],
                                idx["restore_token_order"], idx["expert_ids"], idx["expert_usage_stats"], ws)
         torch.cuda.synchronize()
         check_indices(idx, oracle.create_indices(ids, e))
-    assert int(ws[:4].view(torch.int32).item()) == 0
+        assert int(ws[:4].view(torch.int32).item()) == 0, (i, n, k, e)
