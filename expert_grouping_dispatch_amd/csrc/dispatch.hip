@@ -66,28 +66,27 @@ __device__ __forceinline__ int mx_scale_exponent(uint32_t amax) {
   return se < -127 ? -127 : se;
 }
 
-// E2M1 nibble of one bf16 element for a block scaled by mul = 2^-se.
-// a = |x| * 2^-se is exact whenever it is >= 2^-126, and smaller values
-// round to code 0 either way.  On [0,2) the E2M1 grid has step 0.5, on
-// [2,4) step 1, on [4,8) step 2 (6 is the last code): rounding a / step to
-// an integer with ties to even is the nearest code, ties to the even code.
-__device__ __forceinline__ uint32_t e2m1_nibble(uint32_t bits, float mul) {
-  const float a = __uint_as_float((bits & 0x7FFFu) << 16) * mul;
-  float r;
-  uint32_t base;
-  if (a < 2.0f) {
-    r = __builtin_rintf(a * 2.0f);
-    base = 0;
-  } else if (a < 4.0f) {
-    r = __builtin_rintf(a);
-    base = 2;
-  } else {
-    r = __builtin_rintf(a * 0.5f);
-    base = 4;
-  }
-  uint32_t c = uint32_t(r) + base;
-  c = c > 7u ? 7u : c;
-  return c | ((bits >> 12) & 8u);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Four packed E2M1 bytes from four bf16 pairs with the gfx950 scaled
+// conversion (v_cvt_scalef32_pk_fp4_bf16): each byte holds code(x / scale)
+// of its pair, the first element in the low nibble.  Its rounding (nearest,
+// ties to the even code, saturation at 6, sign kept on zero) equals the
+// E2M1 rule of this dispatch for every finite bf16 value |x| < 8 * scale,
+// which covers every element of a block whose scale comes from the block
+// maximum.
+__device__ __forceinline__ uint32_t e2m1_word(const uint32_t* w, float scale) {
+  uint32_t r = 0u;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, w[0]), scale, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, w[1]), scale, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, w[2]), scale, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, w[3]), scale, 3);
+  return r;
+}
+
+// 2^se as an fp32 value for se in [-127, 127] (2^-127 is the subnormal 0x00400000).
+__device__ __forceinline__ float pow2_f32(int se) {
+  return __uint_as_float(se >= -126 ? uint32_t(se + 127) << 23 : 0x00400000u);
 }
 
 }  // namespace
@@ -178,19 +177,12 @@ __global__ __launch_bounds__(kMxThreads) void k_dispatch_mxfp4(
 #pragma unroll
       for (int i = 0; i < 16; ++i) amax = max(amax, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
       const int se = mx_scale_exponent<kEven>(amax);
-      const float mul = __uint_as_float(uint32_t(127 - se) << 23);
-      uint32_t packed[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t byte =
-            e2m1_nibble(w[i] & 0xFFFFu, mul) | (e2m1_nibble(w[i] >> 16, mul) << 4);
-        packed[i / 4] |= byte << (8 * (i % 4));
-      }
+      const float scale = pow2_f32(se);
       u32x4 pv;
-      pv.x = packed[0];
-      pv.y = packed[1];
-      pv.z = packed[2];
-      pv.w = packed[3];
+      pv.x = e2m1_word(w + 0, scale);
+      pv.y = e2m1_word(w + 4, scale);
+      pv.z = e2m1_word(w + 8, scale);
+      pv.w = e2m1_word(w + 12, scale);
       const uint8_t sbyte = uint8_t(se + 127);
       const int nj = K > 0 ? K : n;
 #pragma unroll

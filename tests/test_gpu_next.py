@@ -110,6 +110,37 @@ def test_mxfp4_even_special_blocks(flags):
     _mxfp4_case(xb, ids, 5, 3, flags)
 
 
+def _every_finite_blocks(seed, h):
+    """Blocks of 32 bf16 values covering every finite pattern under every
+    block maximum exponent B (0..254): each block holds one anchor of
+    exponent B plus 31 patterns of exponent <= B, both signs, so each finite
+    value is quantized against every scale that a block containing it can
+    have."""
+    g = np.random.default_rng(seed)
+    mags = np.arange(0x7F80, dtype=np.uint16)
+    blocks = []
+    for b in range(255):
+        vals = np.concatenate([mags[: (b + 1) << 7], mags[: (b + 1) << 7] | 0x8000]).astype(np.uint16)
+        g.shuffle(vals)
+        n = -(-vals.size // 31)
+        vals = np.concatenate([vals, g.choice(vals, n * 31 - vals.size)]).reshape(n, 31)
+        anchor = ((np.uint16(b) << 7) | (g.integers(0, 2, n) << 15)).astype(np.uint16)
+        blk = np.concatenate([anchor[:, None], vals], axis=1)
+        blocks.append(np.take_along_axis(blk, np.argsort(g.random((n, 32)), axis=1), axis=1))
+    allb = np.concatenate(blocks)
+    allb = np.concatenate([allb, allb[: (-allb.shape[0]) % (h // 32)]])
+    return allb.reshape(-1, h)
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_mxfp4_every_finite_value_under_every_scale(flags):
+    """8.6M elements: the element rounding and the scale rule, bit-exact,
+    over the whole finite bf16 domain."""
+    xb = _every_finite_blocks(7 + flags, 8192)
+    ids = np.zeros((xb.shape[0], 1), np.int32)
+    _mxfp4_case(xb, ids, 1, 1, flags)
+
+
 def test_mxfp4_packed_full_size_sampled():
     """The outlier workload in even + packed mode, checked on sampled rows."""
     w = workloads.WORKLOADS[2]
