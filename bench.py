@@ -79,7 +79,7 @@ def read_traffic(kernel: str, workload: str):
     return float(m_b.group(1))
 
 
-def cpu_baseline(w, cfg, ids, wts, x, y, target_s: float = 15.0):
+def cpu_baseline(w, cfg, ids, wts, x, y, target_s: float = 20.0):
     """The oracle, as it stands, on a smaller instance of the same workload:
     the first n_s rows (all real), their x rows and the first n_s*k rows of y."""
     import oracle
@@ -97,7 +97,7 @@ def cpu_baseline(w, cfg, ids, wts, x, y, target_s: float = 15.0):
         oracle.combine(yb, wts[:n_s], r["restore_token_order"], w.top_k)
         return time.perf_counter() - t0, r["n_routed"]
 
-    n_s = 16
+    n_s = min(w.real_tokens, 128)   # calibration pass: per-row cost, fixed costs amortised
     dt, v = run(n_s)
     n_s = int(min(w.real_tokens, max(16, n_s * target_s / max(dt, 1e-3))))
     dt, v = run(n_s)
