@@ -79,9 +79,11 @@ def read_traffic(kernel: str, workload: str):
     return float(m_b.group(1))
 
 
-def cpu_baseline(w, cfg, ids, wts, x, y, target_s: float = 20.0):
+def cpu_baseline(w, cfg, ids, wts, x, y, gpu=None, target_s: float = 20.0):
     """The oracle, as it stands, on a smaller instance of the same workload:
-    the first n_s rows (all real), their x rows and the first n_s*k rows of y."""
+    the first n_s rows (all real), their x rows and the first n_s*k rows of y.
+    With `gpu` (this run's device outputs) it also checks them against the
+    oracle on the full routing map and on sampled tokens."""
     import oracle
     import torch
 
@@ -101,10 +103,60 @@ def cpu_baseline(w, cfg, ids, wts, x, y, target_s: float = 20.0):
     dt, v = run(n_s)
     n_s = int(min(w.real_tokens, max(16, n_s * target_s / max(dt, 1e-3))))
     dt, v = run(n_s)
-    return {"value": v / dt, "unit": "token-slots/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n_s} real rows of {w.name} (slots {n_s * w.top_k}, H={w.hidden}, "
-                      f"E={w.n_experts}, k={w.top_k}), whole path mask+indices+dispatch bf16+MXFP4+combine, "
-                      f"{dt:.1f} s, NumPy single-threaded on a {os.cpu_count()}-thread host"}
+    sw = workloads.scaled(w, n_rows=n_s, real_tokens=n_s)
+    nbytes = sum(stage_bytes(sw, v).values())
+    res = {"value": v / dt, "unit": "token-slots/s", "cores": 1, "kind": "oracle",
+           "gbps": round(nbytes / dt / 1e9, 4),
+           "sample": f"first {n_s} real rows of {w.name} (slots {n_s * w.top_k}, H={w.hidden}, "
+                     f"E={w.n_experts}, k={w.top_k}), whole path mask+indices+dispatch bf16+MXFP4+combine, "
+                     f"{dt:.1f} s, NumPy single-threaded on a {os.cpu_count()}-thread host"}
+    if gpu is not None:
+        res["parity_of_this_run"] = parity_sample(oracle, torch, w, ids, wts, x, y, gpu)
+    return res
+
+
+def parity_sample(oracle, torch, w, ids, wts, x, y, gpu, n_tok: int = 48):
+    """This run's device outputs against the oracle: the masked map and every
+    index output in full; dispatch (bf16, MXFP4) and combine rows of seeded
+    sampled tokens, real and padding."""
+    k, h = w.top_k, w.hidden
+
+    def u16(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def u32(t):
+        return t.contiguous().view(torch.int32).cpu().numpy().view(np.uint32)
+
+    m = oracle.mask_routing_padding(ids, w.real_tokens)
+    ok = {"mask": bool(np.array_equal(gpu["ids"].cpu().numpy(), m))}
+    ref = oracle.create_indices(m, w.n_experts)
+    idx = gpu["idx"]
+    ok["indices"] = all(
+        np.array_equal(u32(idx[key]), ref[key].astype(np.uint32))
+        for key in ("token_expert_order", "expert_start_indices", "restore_token_order", "expert_usage_stats")) \
+        and np.array_equal(idx["expert_ids"].cpu().numpy(), ref["expert_ids"].astype(np.int32))
+    g = np.random.default_rng(12345)
+    toks = np.unique(np.concatenate([g.integers(0, w.real_tokens, n_tok),
+                                     g.integers(0, w.n_rows, max(1, n_tok // 8))]))
+    rest = ref["restore_token_order"].reshape(w.n_rows, k)[toks]
+    routed = rest != oracle.SENT
+    xs = u16(x[torch.from_numpy(toks).to(x.device)])
+    pos = torch.from_numpy(rest[routed].astype(np.int64)).to(x.device)
+    src = np.repeat(np.arange(len(toks)), k).reshape(-1, k)[routed]
+    ok["dispatch_bf16"] = bool(np.array_equal(u16(gpu["disp"][pos]), xs[src]))
+    pq, ps = oracle.mxfp4_quantize(xs)
+    ok["dispatch_mxfp4"] = bool(np.array_equal(gpu["q"][pos].cpu().numpy(), pq[src])
+                                and np.array_equal(gpu["sc"][pos].cpu().numpy(), ps[src]))
+    # combine over the sampled tokens: their y rows, gathered at the oracle's positions
+    ys = u16(y[pos]) if pos.numel() else np.zeros((0, h), np.uint16)
+    mini = np.full(rest.shape, oracle.SENT, np.uint32)
+    mini[routed] = np.arange(int(routed.sum()), dtype=np.uint32)
+    want = oracle.combine(ys, wts[toks], mini.reshape(-1), k)
+    got = u16(gpu["comb"][torch.from_numpy(toks).to(x.device)])
+    ok["combine"] = bool(np.array_equal(got, want))
+    ok["tokens_sampled"] = int(len(toks))
+    ok["all"] = all(v for key, v in ok.items() if key != "tokens_sampled")
+    return ok
 
 
 def time_extensions(torch, moe, w, x, y, d_ids, d_w, idx, n_routed, reps):
@@ -149,6 +201,41 @@ def time_extensions(torch, moe, w, x, y, d_ids, d_w, idx, n_routed, reps):
     return res
 
 
+def time_pipelines(torch, calls, bts, n_routed, steps, warmup, scrub=None):
+    """Each single-format pipeline (mask -> indices -> one dispatch -> combine)
+    run as its own loop of `steps` passes, events around every stage.  A
+    stage's writes can still be draining from the memory-side cache when the
+    next kernel starts, so only a pipeline's own loop charges it what it
+    leaves behind."""
+    res = {}
+    for pname, sel in (("bf16", (0, 1, 2, 4)), ("mxfp4", (0, 1, 3, 4))):
+        names = [STAGES[j] for j in sel]
+        fns = [calls[j] for j in sel]
+        for _ in range(warmup):
+            for f in fns:
+                f()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+        for i in range(steps):
+            if scrub is not None:
+                scrub()
+            for j, f in enumerate(fns):
+                ev[i][j].record()
+                f()
+            ev[i][len(fns)].record()
+        torch.cuda.synchronize()
+        per = [ev[i][0].elapsed_time(ev[i][len(fns)]) for i in range(steps)]
+        ms = float(np.mean(per)) if scrub is not None else ev[0][0].elapsed_time(ev[-1][len(fns)]) / steps
+        b = sum(bts[nm] for nm in names)
+        st = {nm: round(float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)])), 4)
+              for j, nm in enumerate(names)}
+        res[pname] = {"ms": round(ms, 4), "ms_median": round(float(np.median(per)), 4),
+                      "ms_min": round(float(np.min(per)), 4), "slots_per_s": n_routed / (ms * 1e-3), "bytes": b,
+                      "gbps": round(b / (ms * 1e-3) / 1e9, 1),
+                      "frac_of_peak": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "stage_ms": st}
+    return res
+
+
 def copy_ceiling(torch, gib: float = 2.0, reps: int = 10) -> float:
     """Read+write GB/s of a plain device-to-device copy (a measured ceiling)."""
     n = int(gib * (1 << 30))
@@ -181,6 +268,10 @@ def main():
                     help="skip timing the extension entry points after the step")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy before the steps (counter calibration)")
+    ap.add_argument("--scrub", choices=("auto", "on", "off"), default="auto",
+                    help="read a 1 GiB buffer between steps, outside the timed events, so that no step "
+                         "finds its inputs in L2 or the 256 MB Infinity Cache (auto: when the working "
+                         "set is under 1 GiB)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -209,8 +300,16 @@ def main():
     disp = moe.alloc_dispatch(s, h, dev)
     q, sc = moe.alloc_dispatch_mxfp4(s, h, dev)
     comb = torch.empty((n, h), dtype=torch.bfloat16, device=dev)
+    work_set = sum(t.numel() * t.element_size() for t in (x, y, d_ids, d_w, disp, q, sc, comb)) + \
+        sum(t.numel() * t.element_size() for t in idx.values() if t is not None)
+    scrub = None
+    if args.scrub == "on" or (args.scrub == "auto" and work_set < (1 << 30)):
+        scrub_buf = torch.empty(1 << 28, dtype=torch.int32, device=dev)
+
+        def scrub():  # a read of 1 GiB evicts L2 and Infinity Cache and leaves no dirty lines
+            scrub_buf.max()
     torch.cuda.synchronize()
-    log("inputs resident")
+    log(f"inputs resident, working set {work_set / 2 ** 20:.1f} MiB, scrub between steps: {scrub is not None}")
 
     def stage_calls():
         return [
@@ -262,6 +361,8 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if scrub is not None:
+            scrub()
         if graph is not None:
             ev[i][0].record()
             graph.replay()
@@ -277,6 +378,8 @@ def main():
     stage_ms = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
                 for j, name in enumerate(STAGES)}
     if graph is not None:  # a replay is one unit: per-stage times come from an eager pass of the same step
+        if scrub is not None:
+            scrub()
         eager = [torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
         for j, c in enumerate(calls):
             eager[j].record()
@@ -284,25 +387,22 @@ def main():
         eager[len(STAGES)].record()
         torch.cuda.synchronize()
         stage_ms = {name: eager[j].elapsed_time(eager[j + 1]) for j, name in enumerate(STAGES)}
-    step_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][len(STAGES)]) for i in range(args.steps)]))
+    per_step = [ev[i][0].elapsed_time(ev[i][len(STAGES)]) for i in range(args.steps)]
+    step_ms = float(np.mean(per_step))
     span_ms = ev[0][0].elapsed_time(ev[-1][len(STAGES)]) / args.steps
     log(f"timed {args.steps} steps: {step_ms:.3f} ms/step (events), span {span_ms:.3f}, wall {wall / args.steps * 1e3:.3f}")
 
     bts = stage_bytes(w, n_routed)
     step_bytes = sum(bts.values())
-    ms_per_step = span_ms
+    # back-to-back steps: the span; scrubbed steps: the mean of the per-step times
+    ms_per_step = span_ms if scrub is None else step_ms
     value = n_routed / (ms_per_step * 1e-3)
     gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     stages = {name: {"ms": round(stage_ms[name], 4), "bytes": bts[name],
                      "gbps": round(bts[name] / (stage_ms[name] * 1e-3) / 1e9, 1)} for name in STAGES}
-    pipelines = {}
-    for pname, disp_stage in (("bf16", "dispatch_bf16"), ("mxfp4", "dispatch_mxfp4")):
-        names = ("mask", "indices", disp_stage, "combine")
-        t = sum(stage_ms[nm] for nm in names)
-        b = sum(bts[nm] for nm in names)
-        pipelines[pname] = {"ms": round(t, 4), "slots_per_s": n_routed / (t * 1e-3),
-                            "gbps": round(b / (t * 1e-3) / 1e9, 1),
-                            "frac_of_peak": round(b / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    pipelines = time_pipelines(torch, calls, bts, n_routed, args.steps, args.warmup, scrub)
+    for pname, pl in pipelines.items():
+        log(f"{pname} pipeline: {pl['ms']:.3f} ms/pass, {pl['gbps']} GB/s ({pl['frac_of_peak'] * 100:.1f}% of peak)")
 
     dom = max(KERNEL_OF_STAGE, key=lambda nm: stage_ms[nm])
     kern = KERNEL_OF_STAGE[dom]
@@ -318,7 +418,9 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(w, cfg, ids, wts, x, y)
+        cpu = cpu_baseline(w, cfg, ids, wts, x, y,
+                           gpu=dict(ids=d_ids, idx=idx, disp=disp, q=q, sc=sc, comb=comb))
+        log(f"parity of this run against the oracle: {cpu['parity_of_this_run']}")
 
     out = {
         "metric": METRIC, "value": value, "unit": "token-slots/s", "n_gpus": 1, "steps": args.steps,
@@ -328,7 +430,10 @@ def main():
                    "top_k": k, "routing": w.routing,
                    "step": "mask+create_indices+dispatch_bf16+dispatch_mxfp4+combine"},
         "gbps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "step_ms_median": round(float(np.median(per_step)), 4), "step_ms_min": round(float(np.min(per_step)), 4),
+        "scrub_between_steps": scrub is not None,
         "copy_ceiling_gbps": None if copy_gbps is None else round(copy_gbps, 1),
+        "frac_of_copy_ceiling": None if copy_gbps is None else round(gbps / copy_gbps, 4),
         "stages": stages, "pipelines": pipelines, "graph_replay": bool(args.graph),
         "extensions": extensions, "roofline": roofline, "cpu_baseline": cpu,
     }
