@@ -139,6 +139,15 @@ def test_real_count_edges(real_case, tp_rank):
     _full_check(ids, w, real, e, x, y, ("bf16", "mxfp4"), tp_rank)
 
 
+@pytest.mark.parametrize("real, tp_rank", [(2 ** 31 - 1, 0), (2 ** 31 - 1, 2 ** 31 - 1), (-2 ** 31, 0),
+                                           (-2 ** 31, 5), (2 ** 31 - 1, 7158278), (150 + 300 * 7158278, 7158278)])
+def test_count_and_rank_extremes(real, tp_rank):
+    """The boundary count - tp_rank * N taken in 64 bits, clamped to [0, N]."""
+    n, k, e, h = 300, 4, 16, 64
+    ids, w, _, x, y = _rand_case(1, n, k, e, h, "garbage")
+    _full_check(ids, w, real, e, x, y, ("bf16", "mxfp4"), tp_rank)
+
+
 CASES = {
     # name: (seed, n, k, e, h, kind)
     "k1": (2, 500, 1, 8, 32, "uniform"),
@@ -158,6 +167,14 @@ CASES = {
     "h_large": (16, 20, 2, 4, 16384, "uniform"),
     "h_ragged_vectors": (17, 30, 3, 6, 32 * 37, "uniform"),
     "k1024_e1024": (18, 6, 1024, 1024, 32, "distinct"),
+    # every register-resident slot count (k <= 8) and the first slot-list k
+    "k3_h96": (19, 311, 3, 9, 96, "distinct"),
+    "k5": (20, 301, 5, 12, 160, "distinct"),
+    "k7": (21, 299, 7, 13, 224, "uniform"),
+    "k9": (22, 205, 9, 40, 64, "distinct"),
+    "k16_garbage": (23, 190, 16, 33, 96, "garbage"),
+    "h24_bf16_only": (24, 77, 4, 6, 24, "uniform"),
+    "h32_one_block": (25, 150, 2, 8, 32, "uniform"),
 }
 
 
