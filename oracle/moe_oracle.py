@@ -19,7 +19,7 @@ blocking, fusion or reordering beyond what the definition states.  Sources
   * combine    -- "Struct_ep_combine_wait" (execute description; Args
                   output_tokens / router_weights)
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   * topk_ids is int32 [N, top_k], viewed flat as slots i = t*top_k + j; a
     slot is routed iff 0 <= id < n_experts (the mask's -1 and any garbage id
     are unrouted).
