@@ -434,3 +434,60 @@ def test_workspace_reuse_across_shapes():
         torch.cuda.synchronize()
         check_indices(idx, oracle.create_indices(ids, e))
         assert int(ws[:4].view(torch.int32).item()) == 0, (i, n, k, e)
+
+
+def test_concurrent_streams_with_separate_workspaces():
+    """Two paths of different shapes run at once on two streams, each with its
+    own workspace and outputs; both match the oracle (the library keeps no
+    state outside the buffers it is given)."""
+    cases = [(41, 30000, 8, 256, 64, "distinct"), (42, 20000, 4, 64, 96, "uniform")]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    runs = []
+    for (seed, n, k, e, h, kind), st in zip(cases, streams):
+        ids, w, real, x, y = _rand_case(seed, n, k, e, h, kind, real=n - 17)
+        runs.append((ids, w, real, e, x, y, st))
+    torch.cuda.synchronize()
+    results = []
+    for _ in range(3):
+        outs = []
+        for ids, w, real, e, x, y, st in runs:
+            with torch.cuda.stream(st):
+                outs.append(_launch_path(ids, w, real, e, x, y, st))
+        torch.cuda.synchronize()
+        results = outs
+        for (ids, w, real, e, x, y, st), res in zip(runs, outs):
+            m, ref = _oracle_front(ids, real, e)
+            np.testing.assert_array_equal(i32(res["ids"]), m)
+            check_indices(res, ref)
+            n, k = ids.shape
+            v = ref["n_routed"]
+            np.testing.assert_array_equal(u16(res["dispatch"][:v]),
+                                          oracle.dispatch(u16(x), ref["token_expert_order"], k, v))
+            wq, wsc = oracle.dispatch_mxfp4(u16(x), ref["token_expert_order"], k, v)
+            np.testing.assert_array_equal(res["q"][:v].cpu().numpy(), wq)
+            np.testing.assert_array_equal(res["scales"][:v].cpu().numpy(), wsc)
+            _check_combine(u16(res["combine"]), oracle.combine(u16(y), w, ref["restore_token_order"], k))
+    assert len(results) == 2
+
+
+def _launch_path(ids, w, real, e, x, y, st):
+    """Every stage enqueued on the current stream `st`, with no host sync."""
+    n, k = ids.shape
+    h = x.shape[1]
+    s = n * k
+    with torch.cuda.stream(st):
+        d_ids = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).to(DEV, non_blocking=False)
+        d_cnt = torch.tensor([real], dtype=torch.int32, device=DEV)
+        d_w = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).to(DEV)
+        idx = mod.alloc_indices(s, e, DEV)
+        mod.moe_mask_padding(d_ids, d_cnt, 0)
+        mod.moe_create_indices(d_ids, e, idx["token_expert_order"], idx["expert_start_indices"],
+                               idx["restore_token_order"], idx["expert_ids"], idx["expert_usage_stats"],
+                               idx["workspace"])
+        out = mod.alloc_dispatch(s, h, DEV)
+        mod.moe_dispatch(x, k, idx["restore_token_order"], out)
+        q, sc = mod.alloc_dispatch_mxfp4(s, h, DEV)
+        mod.moe_dispatch_mxfp4(x, k, idx["restore_token_order"], q, sc)
+        o = torch.empty((n, h), dtype=torch.bfloat16, device=DEV)
+        mod.moe_combine(y, d_w, idx["restore_token_order"], k, o)
+    return dict(ids=d_ids, dispatch=out, q=q, scales=sc, combine=o, **idx)
