@@ -29,7 +29,7 @@ constexpr uint64_t kFlagAggregate = uint64_t(1) << 32;  // count of this chunk o
 constexpr uint64_t kFlagPrefix = uint64_t(2) << 32;     // count of chunks [0, c]
 constexpr uint32_t kSpinLimit = 1u << 20;
 #ifndef MOE_LOOKBACK_WINDOW
-#define MOE_LOOKBACK_WINDOW 8
+#define MOE_LOOKBACK_WINDOW 4
 #endif
 constexpr int kLookbackWindow = MOE_LOOKBACK_WINDOW;
 

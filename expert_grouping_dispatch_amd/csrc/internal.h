@@ -15,7 +15,7 @@ namespace moe {
 #define MOE_IDX_THREADS 512
 #endif
 #ifndef MOE_IDX_ROUNDS
-#define MOE_IDX_ROUNDS 8
+#define MOE_IDX_ROUNDS 4
 #endif
 constexpr int kIdxThreads = MOE_IDX_THREADS;
 constexpr int kIdxWaves = kIdxThreads / 64;

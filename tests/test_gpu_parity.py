@@ -175,6 +175,10 @@ CASES = {
     "k16_garbage": (23, 190, 16, 33, 96, "garbage"),
     "h24_bf16_only": (24, 77, 4, 6, 24, "uniform"),
     "h32_one_block": (25, 150, 2, 8, 32, "uniform"),
+    # around the one-workgroup limit of the index stage (2048 slots) and two chunks
+    "s2048_one_workgroup": (26, 256, 8, 256, 32, "distinct"),
+    "s2049_two_chunks": (27, 2049, 1, 16, 32, "uniform"),
+    "s4097": (28, 4097, 1, 300, 32, "uniform"),
 }
 
 
