@@ -85,14 +85,18 @@ template <int K, bool kEpilogue>
 __global__ __launch_bounds__(kCombineMaxThreads) void k_combine(
     const u32x4* __restrict__ y, const float* __restrict__ w, const uint32_t* __restrict__ restore,
     int64_t n_rows, int h16, int top_k, float scale, const u32x4* __restrict__ residual,
-    u32x4* __restrict__ out, uint32_t limit) {
+    u32x4* __restrict__ out, uint32_t limit, RowSplit rs) {
   __shared__ uint32_t s_pos[K > 0 ? 1 : kMaxTopK];
   __shared__ float s_w[K > 0 ? 1 : kMaxTopK];
   __shared__ int s_n;
   constexpr int KR = K > 0 ? K : 1;
   constexpr int kRows = K > 0 ? K : kBatch;  // rows loaded at once
   const int nthreads = blockDim.x;
-  for (int64_t t = blockIdx.x; t < n_rows; t += gridDim.x) {
+  const int64_t items = n_rows * rs.split;
+  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+    const int64_t t = rs.split == 1 ? item : item / rs.split;
+    const int lo = int(item - t * rs.split) * rs.len;  // this workgroup's vectors [lo, hi)
+    const int hi = min(h16, lo + rs.len);
     uint32_t pos[KR];
     float wt[KR];
     int n = 0;
@@ -101,7 +105,7 @@ __global__ __launch_bounds__(kCombineMaxThreads) void k_combine(
     else
       n = gather_routed(restore, w, t, top_k, limit, s_pos, s_w, &s_n);
     u32x4* dst = out + t * h16;
-    for (int c0 = threadIdx.x; c0 < h16; c0 += nthreads * kCombineUnroll) {
+    for (int c0 = lo + int(threadIdx.x); c0 < hi; c0 += nthreads * kCombineUnroll) {
       float acc[kCombineUnroll][8];
 #pragma unroll
       for (int u = 0; u < kCombineUnroll; ++u)
@@ -118,7 +122,7 @@ __global__ __launch_bounds__(kCombineMaxThreads) void k_combine(
 #pragma unroll
             for (int u = 0; u < kCombineUnroll; ++u) {
               const int c = c0 + u * nthreads;
-              if (c < h16) v[u][jj] = load_y(row + c);
+              if (c < hi) v[u][jj] = load_y(row + c);
             }
           }
         }
@@ -129,14 +133,14 @@ __global__ __launch_bounds__(kCombineMaxThreads) void k_combine(
             const float wj = K > 0 ? wt[jj] : s_w[j0 + jj];
 #pragma unroll
             for (int u = 0; u < kCombineUnroll; ++u)
-              if (c0 + u * nthreads < h16) accumulate(acc[u], v[u][jj], wj);
+              if (c0 + u * nthreads < hi) accumulate(acc[u], v[u][jj], wj);
           }
         }
       }
 #pragma unroll
       for (int u = 0; u < kCombineUnroll; ++u) {
         const int c = c0 + u * nthreads;
-        if (c < h16) {
+        if (c < hi) {
           if constexpr (kEpilogue) epilogue(acc[u], scale, residual, t * h16 + c);
           u32x4 o;
           o.x = bf16_rne(acc[u][0]) | (bf16_rne(acc[u][1]) << 16);
@@ -158,12 +162,14 @@ template <int K>
 hipError_t launch_k(const u32x4* y, const float* w, const uint32_t* restore, int64_t n_rows,
                     int h16, int top_k, bool epi, float scale, const u32x4* residual, u32x4* out,
                     uint32_t limit, hipStream_t s) {
+  const RowSplit rs = row_split(n_rows, h16, 128);
+  const dim3 grid(row_grid(n_rows * rs.split)), block(combine_threads(rs.len));
   if (epi)
-    hipLaunchKernelGGL((k_combine<K, true>), dim3(row_grid(n_rows)), dim3(combine_threads(h16)), 0,
-                       s, y, w, restore, n_rows, h16, top_k, scale, residual, out, limit);
+    hipLaunchKernelGGL((k_combine<K, true>), grid, block, 0, s, y, w, restore, n_rows, h16, top_k,
+                       scale, residual, out, limit, rs);
   else
-    hipLaunchKernelGGL((k_combine<K, false>), dim3(row_grid(n_rows)), dim3(combine_threads(h16)),
-                       0, s, y, w, restore, n_rows, h16, top_k, scale, residual, out, limit);
+    hipLaunchKernelGGL((k_combine<K, false>), grid, block, 0, s, y, w, restore, n_rows, h16, top_k,
+                       scale, residual, out, limit, rs);
   return hipGetLastError();
 }
 

@@ -96,11 +96,15 @@ __device__ __forceinline__ float pow2_f32(int se) {
 template <int K>
 __global__ __launch_bounds__(kDispatchThreads) void k_dispatch_bf16(
     const u32x4* __restrict__ x, int64_t n_rows, int h16, int top_k,
-    const uint32_t* __restrict__ restore, u32x4* __restrict__ out, uint32_t limit) {
+    const uint32_t* __restrict__ restore, u32x4* __restrict__ out, uint32_t limit, RowSplit rs) {
   __shared__ uint32_t s_pos[K > 0 ? 1 : kMaxTopK];
   __shared__ int s_n;
   constexpr int KR = K > 0 ? K : 1;
-  for (int64_t t = blockIdx.x; t < n_rows; t += gridDim.x) {
+  const int64_t items = n_rows * rs.split;
+  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+    const int64_t t = rs.split == 1 ? item : item / rs.split;
+    const int lo = int(item - t * rs.split) * rs.len;  // this workgroup's vectors [lo, hi)
+    const int hi = min(h16, lo + rs.len);
     uint32_t pos[KR];
     float unused[KR];
     int n;
@@ -113,12 +117,12 @@ __global__ __launch_bounds__(kDispatchThreads) void k_dispatch_bf16(
       n = gather_routed(restore, nullptr, t, top_k, limit, s_pos, nullptr, &s_n);
     }
     const u32x4* src = x + t * h16;
-    for (int c0 = threadIdx.x; n > 0 && c0 < h16; c0 += kDispatchThreads * kLoadsInFlight) {
+    for (int c0 = lo + int(threadIdx.x); n > 0 && c0 < hi; c0 += kDispatchThreads * kLoadsInFlight) {
       u32x4 v[kLoadsInFlight];
 #pragma unroll
       for (int u = 0; u < kLoadsInFlight; ++u) {
         const int c = c0 + u * kDispatchThreads;
-        if (c < h16) v[u] = load_vec<MOE_DISPATCH_NT_LOAD>(src + c);
+        if (c < hi) v[u] = load_vec<MOE_DISPATCH_NT_LOAD>(src + c);
       }
       const int nj = K > 0 ? K : n;
 #pragma unroll
@@ -129,7 +133,7 @@ __global__ __launch_bounds__(kDispatchThreads) void k_dispatch_bf16(
 #pragma unroll
         for (int u = 0; u < kLoadsInFlight; ++u) {
           const int c = c0 + u * kDispatchThreads;
-          if (c < h16) store_vec<MOE_DISPATCH_NT_STORE>(dst + c, v[u]);
+          if (c < hi) store_vec<MOE_DISPATCH_NT_STORE>(dst + c, v[u]);
         }
       }
     }
@@ -145,12 +149,16 @@ template <int K, bool kEven, bool kPacked>
 __global__ __launch_bounds__(kMxThreads) void k_dispatch_mxfp4(
     const u32x4* __restrict__ x, int64_t n_rows, int h16, int top_k,
     const uint32_t* __restrict__ restore, uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
-    uint32_t limit) {
+    uint32_t limit, RowSplit rs) {
   __shared__ uint32_t s_pos[K > 0 ? 1 : kMaxTopK];
   __shared__ int s_n;
   constexpr int KR = K > 0 ? K : 1;
   const int nblk = h16 / 4;
-  for (int64_t t = blockIdx.x; t < n_rows; t += gridDim.x) {
+  const int64_t items = n_rows * rs.split;
+  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+    const int64_t t = rs.split == 1 ? item : item / rs.split;
+    const int lo = int(item - t * rs.split) * rs.len;  // this workgroup's blocks [lo, hi)
+    const int hi = min(nblk, lo + rs.len);
     uint32_t pos[KR];
     float unused[KR];
     int n;
@@ -163,7 +171,7 @@ __global__ __launch_bounds__(kMxThreads) void k_dispatch_mxfp4(
       n = gather_routed(restore, nullptr, t, top_k, limit, s_pos, nullptr, &s_n);
     }
     const u32x4* src = x + t * h16;
-    for (int b = threadIdx.x; n > 0 && b < nblk; b += kMxThreads) {
+    for (int b = lo + int(threadIdx.x); n > 0 && b < hi; b += kMxThreads) {
       uint32_t w[16];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -225,8 +233,9 @@ template <int K>
 struct LaunchBf16 {
   static hipError_t run(const u32x4* x, int64_t n_rows, int h16, int top_k, const uint32_t* restore,
                         u32x4* out, uint32_t limit, hipStream_t s) {
-    hipLaunchKernelGGL(k_dispatch_bf16<K>, dim3(row_grid(n_rows)), dim3(kDispatchThreads), 0, s, x,
-                       n_rows, h16, top_k, restore, out, limit);
+    const RowSplit rs = row_split(n_rows, h16, kDispatchThreads / 2);
+    hipLaunchKernelGGL(k_dispatch_bf16<K>, dim3(row_grid(n_rows * rs.split)), dim3(kDispatchThreads),
+                       0, s, x, n_rows, h16, top_k, restore, out, limit, rs);
     return hipGetLastError();
   }
 };
@@ -237,8 +246,9 @@ struct LaunchMxfp4 {
   static hipError_t go(const u32x4* x, int64_t n_rows, int h16, int top_k,
                        const uint32_t* restore, uint8_t* q, uint8_t* scales, uint32_t limit,
                        hipStream_t s) {
-    hipLaunchKernelGGL((k_dispatch_mxfp4<K, kEven, kPacked>), dim3(row_grid(n_rows)),
-                       dim3(kMxThreads), 0, s, x, n_rows, h16, top_k, restore, q, scales, limit);
+    const RowSplit rs = row_split(n_rows, h16 / 4, kMxThreads / 8);
+    hipLaunchKernelGGL((k_dispatch_mxfp4<K, kEven, kPacked>), dim3(row_grid(n_rows * rs.split)),
+                       dim3(kMxThreads), 0, s, x, n_rows, h16, top_k, restore, q, scales, limit, rs);
     return hipGetLastError();
   }
   static hipError_t run(const u32x4* x, int64_t n_rows, int h16, int top_k, const uint32_t* restore,

@@ -16,6 +16,27 @@ inline uint32_t row_grid(int64_t n_rows) {
   return uint32_t(n_rows < kMaxRowBlocks ? n_rows : kMaxRowBlocks);
 }
 
+// With few rows, one workgroup per row leaves most CUs idle and each
+// workgroup moves a whole row alone.  Then each row is cut into `split` parts
+// of `len` units (16-byte vectors, or MXFP4 blocks), one workgroup per part,
+// aiming at about kRowSplitTarget workgroups and parts of at least
+// `min_len` units.  Large inputs keep split = 1.
+constexpr int64_t kRowSplitTarget = 1024;
+struct RowSplit {
+  int split;  // parts per row
+  int len;    // units per part (the last part may be shorter)
+};
+inline RowSplit row_split(int64_t n_rows, int units, int min_len) {
+  int split = 1;
+  if (n_rows > 0 && n_rows < kRowSplitTarget) {
+    const int64_t want = (kRowSplitTarget + n_rows - 1) / n_rows;
+    const int64_t most = units / min_len;
+    split = int(want < most ? want : most);
+    if (split < 1) split = 1;
+  }
+  return RowSplit{split, (units + split - 1) / split};
+}
+
 // Positions >= limit are skipped; limit <= 0xFFFFFFFF so the sentinel is
 // always skipped.
 inline uint32_t position_limit(int64_t rows) {

@@ -179,6 +179,9 @@ CASES = {
     "s2048_one_workgroup": (26, 256, 8, 256, 32, "distinct"),
     "s2049_two_chunks": (27, 2049, 1, 16, 32, "uniform"),
     "s4097": (28, 4097, 1, 300, 32, "uniform"),
+    # few rows: each row is cut across several workgroups (ragged last part; slot-list top_k)
+    "split_rows_ragged": (29, 100, 3, 20, 8000, "uniform"),
+    "split_rows_k10": (30, 50, 10, 64, 4096, "distinct"),
 }
 
 
