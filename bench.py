@@ -201,16 +201,25 @@ def time_extensions(torch, moe, w, x, y, d_ids, d_w, idx, n_routed, reps):
     return res
 
 
-def time_pipelines(torch, calls, bts, n_routed, steps, warmup, scrub=None):
+def time_pipelines(torch, calls, bts, n_routed, steps, warmup, scrub=None, fused_front=None):
     """Each single-format pipeline (mask -> indices -> one dispatch -> combine)
     run as its own loop of `steps` passes, events around every stage.  A
     stage's writes can still be draining from the memory-side cache when the
     next kernel starts, so only a pipeline's own loop charges it what it
-    leaves behind."""
+    leaves behind.  With fused_front (the one-call mask + indices), the two
+    pipelines are also timed with it in place of the first two calls."""
     res = {}
-    for pname, sel in (("bf16", (0, 1, 2, 4)), ("mxfp4", (0, 1, 3, 4))):
-        names = [STAGES[j] for j in sel]
-        fns = [calls[j] for j in sel]
+    plans = [("bf16", [(STAGES[j], calls[j]) for j in (0, 1, 2, 4)]),
+             ("mxfp4", [(STAGES[j], calls[j]) for j in (0, 1, 3, 4)])]
+    if fused_front is not None:
+        plans += [("bf16_fused_front", [("mask_indices", fused_front), ("dispatch_bf16", calls[2]),
+                                        ("combine", calls[4])]),
+                  ("mxfp4_fused_front", [("mask_indices", fused_front), ("dispatch_mxfp4", calls[3]),
+                                         ("combine", calls[4])])]
+    bts = dict(bts, mask_indices=bts["mask"] + bts["indices"])
+    for pname, plan in plans:
+        names = [nm for nm, _ in plan]
+        fns = [f for _, f in plan]
         for _ in range(warmup):
             for f in fns:
                 f()
@@ -400,7 +409,12 @@ def main():
     gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     stages = {name: {"ms": round(stage_ms[name], 4), "bytes": bts[name],
                      "gbps": round(bts[name] / (stage_ms[name] * 1e-3) / 1e9, 1)} for name in STAGES}
-    pipelines = time_pipelines(torch, calls, bts, n_routed, args.steps, args.warmup, scrub)
+    def fused_front():
+        moe.moe_mask_create_indices(d_ids, d_cnt, 0, e, idx["token_expert_order"], idx["expert_start_indices"],
+                                    idx["restore_token_order"], idx["expert_ids"], idx["expert_usage_stats"],
+                                    idx["workspace"])
+
+    pipelines = time_pipelines(torch, calls, bts, n_routed, args.steps, args.warmup, scrub, fused_front)
     for pname, pl in pipelines.items():
         log(f"{pname} pipeline: {pl['ms']:.3f} ms/pass, {pl['gbps']} GB/s ({pl['frac_of_peak'] * 100:.1f}% of peak)")
 

@@ -9,6 +9,7 @@ the library is missing, importing this package fails.
 
     mask -> moe_mask_padding(routing_map, real_token_count, tp_rank)        int32 or int64 map
     idx  -> moe_create_indices(topk_ids, n_experts, *outputs, workspace[, scales_offset, scales_align])
+    both -> moe_mask_create_indices(routing_map, real_token_count, tp_rank, n_experts, *outputs, workspace, ...)
     out  -> moe_dispatch(input_tokens, top_k, restore_token_order, out)
             moe_dispatch_mxfp4(input_tokens, top_k, restore_token_order, out_q, out_scales, flags)
     out  -> moe_combine(y, router_weights, restore_token_order, top_k, output_tokens)
@@ -23,7 +24,7 @@ import torch
 
 __all__ = [
     "SENTINEL", "MoeError", "LIB_PATH", "lib",
-    "moe_mask_padding", "moe_create_indices", "moe_create_indices_workspace_bytes",
+    "moe_mask_padding", "moe_create_indices", "moe_create_indices_workspace_bytes", "moe_mask_create_indices",
     "moe_dispatch", "moe_dispatch_mxfp4", "moe_combine", "moe_combine_epilogue", "moe_error_string",
     "MXFP4_EVEN_SCALE", "MXFP4_PACKED_ROWS",
     "alloc_indices", "alloc_dispatch", "alloc_dispatch_mxfp4",
@@ -36,7 +37,7 @@ MXFP4_PACKED_ROWS = 2  # flags bit of moe_dispatch_mxfp4: payload and scales in 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_route.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m expert_grouping_dispatch_amd.build_lib`")
+    raise ImportError(f"{LIB_PATH} is not built; run `python expert_grouping_dispatch_amd/build_lib.py`")
 
 # torch is imported first so the library binds to the HIP runtime torch already loaded.
 lib = ctypes.CDLL(LIB_PATH)
@@ -51,6 +52,9 @@ lib.moe_create_indices_workspace_bytes.argtypes = [_i64, _i32]
 lib.moe_create_indices_workspace_bytes.restype = _sz
 for _f in (lib.moe_create_indices, lib.moe_create_indices_i64):
     _f.argtypes = [_p, _i64, _i32, _p, _p, _p, _p, _p, _p, _u32, _p, _sz, _p]
+    _f.restype = ctypes.c_int
+for _f in (lib.moe_mask_create_indices, lib.moe_mask_create_indices_i64):
+    _f.argtypes = [_p, _i64, _i32, _p, _i32, _i32, _p, _p, _p, _p, _p, _p, _u32, _p, _sz, _p]
     _f.restype = ctypes.c_int
 lib.moe_dispatch.argtypes = [_p, _i64, _i32, _i32, _p, _p, _i64, _p]
 lib.moe_dispatch.restype = ctypes.c_int
@@ -154,6 +158,17 @@ def moe_create_indices(topk_ids: torch.Tensor, n_experts: int, token_expert_orde
     dt = _id_dtype(topk_ids, "topk_ids")
     _need(topk_ids, "topk_ids", dt, dev)
     s = topk_ids.numel()
+    soff = _index_outputs(dev, s, n_experts, token_expert_order, expert_start_indices, restore_token_order,
+                          expert_ids, expert_usage_stats, workspace, scales_offset)
+    fn = lib.moe_create_indices if dt == torch.int32 else lib.moe_create_indices_i64
+    with torch.cuda.device(dev):
+        _check(fn(_ptr(topk_ids), s, int(n_experts), _ptr(token_expert_order), _ptr(expert_start_indices),
+                  _ptr(restore_token_order), _ptr(expert_ids), _ptr(expert_usage_stats), soff,
+                  int(scales_align), _ptr(workspace), workspace.numel(), _stream(dev)), "moe_create_indices")
+
+
+def _index_outputs(dev, s, n_experts, token_expert_order, expert_start_indices, restore_token_order,
+                   expert_ids, expert_usage_stats, workspace, scales_offset):
     for name, t, odt, n in (("token_expert_order", token_expert_order, torch.uint32, s),
                             ("expert_start_indices", expert_start_indices, torch.uint32, n_experts + 1),
                             ("restore_token_order", restore_token_order, torch.uint32, s),
@@ -163,17 +178,36 @@ def moe_create_indices(topk_ids: torch.Tensor, n_experts: int, token_expert_orde
         if t.numel() != n:
             raise ValueError(f"{name} must have {n} elements, has {t.numel()}")
     _need(workspace, "workspace", torch.uint8, dev)
-    soff = ctypes.c_void_p(0)
-    if scales_offset is not None:
-        _need(scales_offset, "scales_offset", torch.uint32, dev)
-        if scales_offset.numel() != n_experts + 1:
-            raise ValueError(f"scales_offset must have {n_experts + 1} elements")
-        soff = _ptr(scales_offset)
-    fn = lib.moe_create_indices if dt == torch.int32 else lib.moe_create_indices_i64
+    if scales_offset is None:
+        return ctypes.c_void_p(0)
+    _need(scales_offset, "scales_offset", torch.uint32, dev)
+    if scales_offset.numel() != n_experts + 1:
+        raise ValueError(f"scales_offset must have {n_experts + 1} elements")
+    return _ptr(scales_offset)
+
+
+def moe_mask_create_indices(routing_map: torch.Tensor, real_token_count: torch.Tensor, tp_rank: int,
+                            n_experts: int, token_expert_order: torch.Tensor,
+                            expert_start_indices: torch.Tensor, restore_token_order: torch.Tensor,
+                            expert_ids: torch.Tensor, expert_usage_stats: torch.Tensor,
+                            workspace: torch.Tensor, scales_offset: torch.Tensor = None,
+                            scales_align: int = 128) -> None:
+    """moe_mask_padding then moe_create_indices on the masked map, in one call."""
+    dev = _device_of(routing_map)
+    dt = _id_dtype(routing_map, "routing_map")
+    _need(routing_map, "routing_map", dt, dev)
+    _need(real_token_count, "real_token_count", torch.int32, dev)
+    if routing_map.dim() != 2 or real_token_count.numel() != 1:
+        raise ValueError("routing_map must be [N, top_k] and real_token_count [1]")
+    n, k = routing_map.shape
+    soff = _index_outputs(dev, n * k, n_experts, token_expert_order, expert_start_indices,
+                          restore_token_order, expert_ids, expert_usage_stats, workspace, scales_offset)
+    fn = lib.moe_mask_create_indices if dt == torch.int32 else lib.moe_mask_create_indices_i64
     with torch.cuda.device(dev):
-        _check(fn(_ptr(topk_ids), s, int(n_experts), _ptr(token_expert_order), _ptr(expert_start_indices),
-                  _ptr(restore_token_order), _ptr(expert_ids), _ptr(expert_usage_stats), soff,
-                  int(scales_align), _ptr(workspace), workspace.numel(), _stream(dev)), "moe_create_indices")
+        _check(fn(_ptr(routing_map), n, k, _ptr(real_token_count), int(tp_rank), int(n_experts),
+                  _ptr(token_expert_order), _ptr(expert_start_indices), _ptr(restore_token_order),
+                  _ptr(expert_ids), _ptr(expert_usage_stats), soff, int(scales_align), _ptr(workspace),
+                  workspace.numel(), _stream(dev)), "moe_mask_create_indices")
 
 
 def alloc_dispatch(n_slots: int, hidden: int, device) -> torch.Tensor:

@@ -1,6 +1,6 @@
 """Build the HIP C-ABI library ``libmoe_route.so`` in-tree for gfx950.
 
-    python -m expert_grouping_dispatch_amd.build_lib
+    python expert_grouping_dispatch_amd/build_lib.py
 
 Compiles every ``csrc/*.hip`` with hipcc (device code for gfx950 only) and
 links them into ``expert_grouping_dispatch_amd/libmoe_route.so``.

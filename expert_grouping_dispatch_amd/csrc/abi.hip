@@ -56,7 +56,7 @@ int create_indices(const IdT* topk_ids, int64_t n_slots, int32_t n_experts,
                    uint32_t* token_expert_order, uint32_t* expert_start_indices,
                    uint32_t* restore_token_order, int32_t* expert_ids,
                    uint32_t* expert_usage_stats, uint32_t* scales_offset, uint32_t scales_align,
-                   void* workspace, size_t workspace_bytes, void* stream) {
+                   void* workspace, size_t workspace_bytes, moe::PadMask pad, void* stream) {
   if (n_slots < 0 || n_slots > int64_t(0xFFFFFFFEu) || n_experts < 1 || n_experts > MOE_MAX_EXPERTS)
     return MOE_ERR_INVALID_ARGUMENT;
   if (expert_start_indices == nullptr || expert_ids == nullptr || expert_usage_stats == nullptr ||
@@ -79,7 +79,27 @@ int create_indices(const IdT* topk_ids, int64_t n_slots, int32_t n_experts,
   return launched(moe::launch_create_indices(topk_ids, n_slots, n_experts, token_expert_order,
                                              expert_start_indices, restore_token_order, expert_ids,
                                              expert_usage_stats, scales_offset, scales_align,
-                                             workspace, static_cast<hipStream_t>(stream)));
+                                             workspace, pad, static_cast<hipStream_t>(stream)));
+}
+
+// Stages 1 and 2 in one call: the mask's checks, then the index checks on
+// the n_rows * top_k slots of the map.
+template <typename IdT>
+int mask_create_indices(IdT* routing_map, int64_t n_rows, int32_t top_k,
+                        const int32_t* real_token_count, int32_t tp_rank, int32_t n_experts,
+                        uint32_t* token_expert_order, uint32_t* expert_start_indices,
+                        uint32_t* restore_token_order, int32_t* expert_ids,
+                        uint32_t* expert_usage_stats, uint32_t* scales_offset,
+                        uint32_t scales_align, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (!slots_ok(n_rows, top_k) || tp_rank < 0 || real_token_count == nullptr ||
+      !aligned(real_token_count, 4))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return create_indices<IdT>(routing_map, n_rows * top_k, n_experts, token_expert_order,
+                             expert_start_indices, restore_token_order, expert_ids,
+                             expert_usage_stats, scales_offset, scales_align, workspace,
+                             workspace_bytes, moe::PadMask{real_token_count, top_k, tp_rank},
+                             stream);
 }
 
 int combine(const uint16_t* y, int64_t y_rows, const float* router_weights,
@@ -145,7 +165,8 @@ int moe_create_indices(const int32_t* topk_ids, int64_t n_slots, int32_t n_exper
                        void* stream) {
   return create_indices(topk_ids, n_slots, n_experts, token_expert_order, expert_start_indices,
                         restore_token_order, expert_ids, expert_usage_stats, scales_offset,
-                        scales_align, workspace, workspace_bytes, stream);
+                        scales_align, workspace, workspace_bytes, moe::PadMask{nullptr, 1, 0},
+                        stream);
 }
 
 int moe_create_indices_i64(const int64_t* topk_ids, int64_t n_slots, int32_t n_experts,
@@ -156,7 +177,34 @@ int moe_create_indices_i64(const int64_t* topk_ids, int64_t n_slots, int32_t n_e
                            void* stream) {
   return create_indices(topk_ids, n_slots, n_experts, token_expert_order, expert_start_indices,
                         restore_token_order, expert_ids, expert_usage_stats, scales_offset,
-                        scales_align, workspace, workspace_bytes, stream);
+                        scales_align, workspace, workspace_bytes, moe::PadMask{nullptr, 1, 0},
+                        stream);
+}
+
+int moe_mask_create_indices(int32_t* routing_map, int64_t n_rows, int32_t top_k,
+                            const int32_t* real_token_count, int32_t tp_rank, int32_t n_experts,
+                            uint32_t* token_expert_order, uint32_t* expert_start_indices,
+                            uint32_t* restore_token_order, int32_t* expert_ids,
+                            uint32_t* expert_usage_stats, uint32_t* scales_offset,
+                            uint32_t scales_align, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  return mask_create_indices(routing_map, n_rows, top_k, real_token_count, tp_rank, n_experts,
+                             token_expert_order, expert_start_indices, restore_token_order,
+                             expert_ids, expert_usage_stats, scales_offset, scales_align,
+                             workspace, workspace_bytes, stream);
+}
+
+int moe_mask_create_indices_i64(int64_t* routing_map, int64_t n_rows, int32_t top_k,
+                                const int32_t* real_token_count, int32_t tp_rank,
+                                int32_t n_experts, uint32_t* token_expert_order,
+                                uint32_t* expert_start_indices, uint32_t* restore_token_order,
+                                int32_t* expert_ids, uint32_t* expert_usage_stats,
+                                uint32_t* scales_offset, uint32_t scales_align, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return mask_create_indices(routing_map, n_rows, top_k, real_token_count, tp_rank, n_experts,
+                             token_expert_order, expert_start_indices, restore_token_order,
+                             expert_ids, expert_usage_stats, scales_offset, scales_align,
+                             workspace, workspace_bytes, stream);
 }
 
 int moe_dispatch(const uint16_t* input_tokens, int64_t n_rows, int32_t hidden, int32_t top_k,

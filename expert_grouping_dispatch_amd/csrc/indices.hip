@@ -47,11 +47,33 @@ __device__ __forceinline__ bool is_leader(uint64_t peers) {
   return peers != 0 && __builtin_ctzll(peers) == __lane_id();
 }
 
+// First slot of the padding rows to mask (n_slots when nothing is masked):
+// the boundary count - tp_rank * n_rows, clamped to [0, n_rows], in 64 bits.
+__device__ __forceinline__ int64_t pad_begin(const PadMask& pad, int64_t n_slots) {
+  if (pad.count == nullptr) return n_slots;
+  const int64_t n_rows = n_slots / pad.top_k;
+  int64_t first = int64_t(*pad.count) - int64_t(pad.tp_rank) * n_rows;
+  first = first < 0 ? 0 : (first > n_rows ? n_rows : first);
+  return first * pad.top_k;
+}
+
+// Bucket of slot i; slots at or past pad_from are padding: unrouted, and
+// set to -1 through wmap (the same map, writable) when masking.  Each slot
+// is read and written by the same thread, and no other workgroup of the
+// kernel reads it.
+template <typename IdT>
+__device__ __forceinline__ uint32_t slot_key(const IdT* ids, IdT* wmap, int64_t i, int64_t pad_from,
+                                             uint32_t n_experts) {
+  if (i < pad_from) return bucket_of(ids[i], n_experts);
+  if (wmap != nullptr) wmap[i] = IdT(-1);
+  return n_experts;
+}
+
 // Count the chunk's slots per bucket into hist[0..E] (LDS, zeroed by caller).
 // Only totals are needed here, so plain LDS atomics do.
 template <typename IdT>
-__device__ void chunk_histogram(const IdT* __restrict__ ids, int64_t n_slots, int64_t begin,
-                                uint32_t n_experts, uint32_t* hist) {
+__device__ void chunk_histogram(const IdT* ids, IdT* wmap, int64_t n_slots, int64_t begin,
+                                uint32_t n_experts, uint32_t* hist, int64_t pad_from) {
   const int tid = threadIdx.x;
   uint32_t key[kIdxRounds];
   bool valid[kIdxRounds];
@@ -59,7 +81,7 @@ __device__ void chunk_histogram(const IdT* __restrict__ ids, int64_t n_slots, in
   for (int r = 0; r < kIdxRounds; ++r) {
     const int64_t i = begin + int64_t(r) * kIdxThreads + tid;
     valid[r] = i < n_slots;
-    key[r] = valid[r] ? bucket_of(ids[i], n_experts) : 0u;
+    key[r] = valid[r] ? slot_key(ids, wmap, i, pad_from, n_experts) : 0u;
   }
 #pragma unroll
   for (int r = 0; r < kIdxRounds; ++r)
@@ -80,8 +102,9 @@ struct WaveTile {
 // Load the wave's keys and count them per bucket into its own LDS row
 // whist[wave][0..E] (only this wave touches the row; no atomics).
 template <typename IdT>
-__device__ void wave_counts(const IdT* __restrict__ ids, int64_t n_slots, int64_t begin,
-                            uint32_t n_experts, int nbits, uint32_t* whist, WaveTile& tile) {
+__device__ void wave_counts(const IdT* ids, IdT* wmap, int64_t n_slots, int64_t begin,
+                            uint32_t n_experts, int nbits, uint32_t* whist, WaveTile& tile,
+                            int64_t pad_from) {
   const int lane = __lane_id(), wave = threadIdx.x / kWave;
   const int nb = int(n_experts) + 1;
   uint32_t* my = whist + wave * nb;
@@ -90,7 +113,7 @@ __device__ void wave_counts(const IdT* __restrict__ ids, int64_t n_slots, int64_
   for (int r = 0; r < kIdxRounds; ++r) {
     const int64_t i = tile.wbegin + r * kWave + lane;
     tile.valid[r] = i < n_slots;
-    tile.key[r] = tile.valid[r] ? bucket_of(ids[i], n_experts) : 0u;
+    tile.key[r] = tile.valid[r] ? slot_key(ids, wmap, i, pad_from, n_experts) : 0u;
   }
   for (int b = lane; b < nb; b += kWave) my[b] = 0;
 #pragma unroll
@@ -260,10 +283,11 @@ __device__ uint32_t lookback(const uint64_t* flags, int64_t c, int nb, int b, ui
 // scatter follows in k_index_scatter.
 template <typename IdT>
 __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
-    const IdT* __restrict__ ids, int64_t n_slots, uint32_t n_experts, int nbits,
+    const IdT* ids, int64_t n_slots, uint32_t n_experts, int nbits,
     int64_t n_chunks, IndexWorkspace ws, uint32_t* __restrict__ esi,
     int32_t* __restrict__ expert_ids, uint32_t* __restrict__ stats, uint32_t* __restrict__ soff,
-    uint32_t align, uint32_t* __restrict__ teo, uint32_t* __restrict__ restore) {
+    uint32_t align, uint32_t* __restrict__ teo, uint32_t* __restrict__ restore, PadMask pad,
+    IdT* wmap) {
   extern __shared__ uint32_t lds[];
   __shared__ int64_t s_chunk;
   const int nb = int(n_experts) + 1;
@@ -275,7 +299,7 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
     uint32_t* base = lds + nb;
     uint32_t* whist = lds + 2 * nb;
     WaveTile tile;
-    wave_counts(ids, n_slots, 0, n_experts, nbits, whist, tile);
+    wave_counts(ids, wmap, n_slots, 0, n_experts, nbits, whist, tile, pad_begin(pad, n_slots));
     __syncthreads();
     for (int b = tid; b < nb; b += kIdxThreads) {
       uint32_t t = 0;
@@ -295,7 +319,7 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
   for (int b = tid; b < nb; b += kIdxThreads) hist[b] = 0;
   __syncthreads();
   const int64_t c = s_chunk;
-  chunk_histogram(ids, n_slots, c * kIdxChunk, n_experts, hist);
+  chunk_histogram(ids, wmap, n_slots, c * kIdxChunk, n_experts, hist, pad_begin(pad, n_slots));
   __syncthreads();
 
   for (int b = tid; b < nb; b += kIdxThreads) {
@@ -346,7 +370,9 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scatter(
     if (b < nb) ws.flags[c * nb + b] = 0u;
   }
   WaveTile tile;
-  wave_counts(ids, n_slots, c * kIdxChunk, n_experts, nbits, lds + nb, tile);
+  // the map was masked by k_index_hist, so it is read as it is now
+  wave_counts(ids, static_cast<IdT*>(nullptr), n_slots, c * kIdxChunk, n_experts, nbits, lds + nb,
+              tile, n_slots);
 #pragma unroll
   for (int q = 0; q < kMaxPerThread; ++q) {
     const int b = threadIdx.x + q * kIdxThreads;
@@ -387,21 +413,23 @@ template <typename IdT>
 hipError_t launch_create_indices(const IdT* ids, int64_t n_slots, int n_experts, uint32_t* teo,
                                  uint32_t* esi, uint32_t* restore, int32_t* expert_ids,
                                  uint32_t* stats, uint32_t* soff, uint32_t align, void* wsp,
-                                 hipStream_t s) {
+                                 PadMask pad, hipStream_t s) {
   const int64_t chunks = index_chunks(n_slots);
   const int nb = n_experts + 1;
   const int nbits = 32 - __builtin_clz(uint32_t(n_experts));
   const IndexWorkspace ws = index_workspace_carve(wsp, n_slots, n_experts);
+  // when masking, the map was handed in writable (the fused mask + index call)
+  IdT* wmap = pad.count != nullptr ? const_cast<IdT*>(ids) : nullptr;
   if (chunks == 1) {
     const size_t lds = size_t(2 + kIdxWaves) * nb * sizeof(uint32_t);
     hipLaunchKernelGGL(k_index_hist<IdT>, dim3(1), dim3(kIdxThreads), lds, s, ids, n_slots,
                        uint32_t(n_experts), nbits, chunks, ws, esi, expert_ids, stats, soff, align,
-                       teo, restore);
+                       teo, restore, pad, wmap);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(k_index_hist<IdT>, dim3(uint32_t(chunks)), dim3(kIdxThreads),
                      size_t(nb) * sizeof(uint32_t), s, ids, n_slots, uint32_t(n_experts), nbits,
-                     chunks, ws, esi, expert_ids, stats, soff, align, teo, restore);
+                     chunks, ws, esi, expert_ids, stats, soff, align, teo, restore, pad, wmap);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_index_scatter<IdT>, dim3(uint32_t(chunks)), dim3(kIdxThreads),
@@ -412,9 +440,9 @@ hipError_t launch_create_indices(const IdT* ids, int64_t n_slots, int n_experts,
 
 template hipError_t launch_create_indices<int32_t>(const int32_t*, int64_t, int, uint32_t*,
                                                    uint32_t*, uint32_t*, int32_t*, uint32_t*,
-                                                   uint32_t*, uint32_t, void*, hipStream_t);
+                                                   uint32_t*, uint32_t, void*, PadMask, hipStream_t);
 template hipError_t launch_create_indices<int64_t>(const int64_t*, int64_t, int, uint32_t*,
                                                    uint32_t*, uint32_t*, int32_t*, uint32_t*,
-                                                   uint32_t*, uint32_t, void*, hipStream_t);
+                                                   uint32_t*, uint32_t, void*, PadMask, hipStream_t);
 
 }  // namespace moe

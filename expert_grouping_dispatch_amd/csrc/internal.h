@@ -41,11 +41,20 @@ template <typename IdT>
 hipError_t launch_mask_padding(IdT* ids, int64_t n_rows, int top_k, const int32_t* count,
                                int tp_rank, hipStream_t s);
 
+// Padding rows masked while indexing (the fused mask + index call): rows r
+// with r + tp_rank * (n_slots / top_k) >= *count become -1 in the map and
+// are unrouted.  count == nullptr masks nothing and the map is only read.
+struct PadMask {
+  const int32_t* count;
+  int32_t top_k;
+  int32_t tp_rank;
+};
+
 template <typename IdT>
 hipError_t launch_create_indices(const IdT* ids, int64_t n_slots, int n_experts, uint32_t* teo,
                                  uint32_t* esi, uint32_t* restore, int32_t* expert_ids,
                                  uint32_t* stats, uint32_t* scales_offset, uint32_t scales_align,
-                                 void* ws, hipStream_t s);
+                                 void* ws, PadMask pad, hipStream_t s);
 
 hipError_t launch_dispatch_bf16(const uint16_t* x, int64_t n_rows, int hidden, int top_k,
                                 const uint32_t* restore, uint16_t* out, int64_t out_rows,

@@ -156,6 +156,35 @@ int moe_create_indices_i64(const int64_t* topk_ids, int64_t n_slots, int32_t n_e
                            void* stream);
 
 /*
+ * Stages 1 and 2 in one call, for callers that run them back to back.
+ * ("core.transformer.moe.inference_routing_mask_kernel", mask_routing_padding,
+ *  then "moe_create_indices", as above.)  The results are exactly those of
+ * moe_mask_padding(routing_map, n_rows, top_k, real_token_count, tp_rank)
+ * followed by moe_create_indices on the masked map viewed flat
+ * (n_slots = n_rows * top_k), with one kernel launch fewer: padding slots
+ * are set to -1 in routing_map (in place) and counted as unrouted while the
+ * index is built.  Arguments, layouts, ownership and errors are those of the
+ * two calls; the map must not be read or written by other work while the
+ * call runs.
+ */
+int moe_mask_create_indices(int32_t* routing_map, int64_t n_rows, int32_t top_k,
+                            const int32_t* real_token_count, int32_t tp_rank, int32_t n_experts,
+                            uint32_t* token_expert_order, uint32_t* expert_start_indices,
+                            uint32_t* restore_token_order, int32_t* expert_ids,
+                            uint32_t* expert_usage_stats, uint32_t* scales_offset,
+                            uint32_t scales_align, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* As moe_mask_create_indices for an int64 routing map. */
+int moe_mask_create_indices_i64(int64_t* routing_map, int64_t n_rows, int32_t top_k,
+                                const int32_t* real_token_count, int32_t tp_rank,
+                                int32_t n_experts, uint32_t* token_expert_order,
+                                uint32_t* expert_start_indices, uint32_t* restore_token_order,
+                                int32_t* expert_ids, uint32_t* expert_usage_stats,
+                                uint32_t* scales_offset, uint32_t scales_align, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
  * Stage 3a -- dispatch in bf16.
  * ("Struct_ep_dispatch_async_mxfp4", execute and Args: input_tokens
  *  [num_tokens, hidden_size] are sent to the experts chosen in topk_ids

@@ -25,8 +25,8 @@ def declared_functions():
 def test_header_declares_the_path():
     assert declared_functions() == sorted([
         "moe_error_string", "moe_mask_padding", "moe_mask_padding_i64", "moe_create_indices_workspace_bytes",
-        "moe_create_indices", "moe_create_indices_i64", "moe_dispatch", "moe_dispatch_mxfp4", "moe_combine",
-        "moe_combine_epilogue"])
+        "moe_create_indices", "moe_create_indices_i64", "moe_mask_create_indices", "moe_mask_create_indices_i64",
+        "moe_dispatch", "moe_dispatch_mxfp4", "moe_combine", "moe_combine_epilogue"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -87,6 +87,23 @@ def test_invalid_arguments_rejected_on_host():
         bad = list(args); bad[8] = fake; bad[9] = 2 ** 31
         assert fn(*bad) == 1                                        # aligned offsets would overflow
     assert L.moe_mask_padding_i64(P(260), 4, 2, cnt, 0, None) == 1   # int64 map misaligned
+    ws = mod.moe_create_indices_workspace_bytes(50 * 2, 8)
+    fused = [fake, 50, 2, cnt, 0, 8, fake, fake, fake, fake, fake, None, 0, fake, ws, None]
+    for fn in (L.moe_mask_create_indices, L.moe_mask_create_indices_i64):
+        bad = list(fused); bad[3] = None
+        assert fn(*bad) == 1                                        # null count
+        bad = list(fused); bad[4] = -1
+        assert fn(*bad) == 1                                        # tp_rank < 0
+        bad = list(fused); bad[2] = 0
+        assert fn(*bad) == 1                                        # top_k < 1
+        bad = list(fused); bad[5] = 1025
+        assert fn(*bad) == 1                                        # n_experts too large
+        bad = list(fused); bad[1] = 2 ** 31
+        assert fn(*bad) == 1                                        # slots reach the sentinel
+        bad = list(fused); bad[14] = ws - 1
+        assert fn(*bad) == 2                                        # workspace too small
+    assert L.moe_mask_create_indices_i64(P(260), 50, 2, cnt, 0, 8, fake, fake, fake, fake, fake, None, 0,
+                                         fake, ws, None) == 1       # int64 map misaligned
     assert L.moe_dispatch(fake, 10, 12, 2, fake, fake, 20, None) == 1        # hidden % 8
     assert L.moe_dispatch(P(258), 10, 16, 2, fake, fake, 20, None) == 1      # misaligned x
     assert L.moe_dispatch(fake, 10, 16, 0, fake, fake, 20, None) == 1        # top_k < 1

@@ -13,7 +13,7 @@ BIN = os.path.join(os.path.dirname(__file__), "c_abi", "route_smoke.bin")
 
 def test_plain_c_program_runs_the_path():
     if not os.path.exists(BIN):
-        pytest.fail(f"{BIN} is not built; run `python -m expert_grouping_dispatch_amd.build_lib`")
+        pytest.fail(f"{BIN} is not built; run `python expert_grouping_dispatch_amd/build_lib.py`")
     r = subprocess.run([BIN], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "c-abi ok" in r.stdout

@@ -1,5 +1,6 @@
 """GPU parity of the extensions: aligned scale offsets, int64 routing maps,
-even-mode and packed MXFP4 dispatch, and the fused combine epilogue."""
+even-mode and packed MXFP4 dispatch, the fused combine epilogue, and the
+fused mask + index call."""
 import numpy as np
 import pytest
 import torch
@@ -204,3 +205,74 @@ def test_combine_epilogue_matches_combine_at_identity():
     torch.cuda.synchronize()
     want = oracle.combine_epilogue(u16(y), wts, ref["restore_token_order"], w.top_k, 0.5, u16(res))
     np.testing.assert_array_equal(u16(b), want)
+
+
+# ---------------------------------------------------------------- fused mask + indices
+def _fused(ids, real, tp_rank, e, align=None):
+    d_map = torch.from_numpy(np.ascontiguousarray(ids)).to(DEV)
+    cnt = torch.tensor([real], dtype=torch.int32, device=DEV)
+    idx = mod.alloc_indices(d_map.numel(), e, DEV, scales_offset=align is not None)
+    mod.moe_mask_create_indices(d_map, cnt, tp_rank, e, idx["token_expert_order"], idx["expert_start_indices"],
+                                idx["restore_token_order"], idx["expert_ids"], idx["expert_usage_stats"],
+                                idx["workspace"], idx["scales_offset"], align or 1)
+    torch.cuda.synchronize()
+    return d_map, idx
+
+
+def _check_fused(ids, real, tp_rank, e, align=None):
+    d_map, idx = _fused(ids, real, tp_rank, e, align)
+    m = oracle.mask_routing_padding(ids, real, tp_rank)
+    np.testing.assert_array_equal(d_map.cpu().numpy(), m)
+    ref = oracle.create_indices(m, e, scales_align=align)
+    check_indices(idx, ref)
+    if align is not None:
+        np.testing.assert_array_equal(u32(idx["scales_offset"]), ref["scales_offset"])
+    assert int(idx["workspace"][:4].view(torch.int32).item()) == 0
+
+
+@pytest.mark.parametrize("cfg", range(len(workloads.WORKLOADS)))
+def test_fused_mask_indices_on_workloads(cfg):
+    w = workloads.WORKLOADS[cfg]
+    ids, _, real = workloads.make_routing(w, cfg)
+    _check_fused(ids, real, 0, w.n_experts)
+
+
+@pytest.mark.parametrize("n,k,e,real,tp_rank", [
+    (256, 8, 256, 97, 0),            # one workgroup (2048 slots)
+    (257, 8, 256, 97, 0),            # two chunks
+    (3000, 4, 16, 0, 0),             # everything masked
+    (3000, 4, 16, 3000, 0),          # nothing masked
+    (3000, 4, 16, -7, 0),
+    (3000, 4, 16, 3000 + 1234, 1),   # second shard: boundary 1234
+    (3000, 4, 16, 2 ** 31 - 1, 715827),
+    (40000, 8, 1024, 39999, 0),
+    (1, 1, 1, 1, 0),
+    (0, 4, 8, 0, 0),
+])
+def test_fused_mask_indices_edges(n, k, e, real, tp_rank):
+    g = np.random.default_rng(n + k + e)
+    ids = g.integers(-2, e + 2, size=(n, k)).astype(np.int32)
+    _check_fused(ids, real, tp_rank, e)
+
+
+@pytest.mark.parametrize("align", [1, 128])
+def test_fused_mask_indices_int64_and_offsets(align):
+    n, k, e, real = 5000, 8, 256, 4321
+    g = np.random.default_rng(7)
+    pool = np.array([-1, 2 ** 33 + 1, e, -(2 ** 40)] + list(range(e)), np.int64)
+    ids = g.choice(pool, size=(n, k))
+    _check_fused(ids, real, 0, e, align)
+
+
+def test_fused_equals_separate_calls():
+    """Same map bytes and index outputs as moe_mask_padding then moe_create_indices."""
+    w = workloads.WORKLOADS[4]
+    ids, _, real = workloads.make_routing(w, 4)
+    d_map, fused = _fused(ids, real, 0, w.n_experts)
+    d_sep = torch.from_numpy(ids).to(DEV)
+    mod.moe_mask_padding(d_sep, torch.tensor([real], dtype=torch.int32, device=DEV), 0)
+    sep = _indices(d_sep, w.n_experts)
+    assert torch.equal(d_map, d_sep)
+    for key in ("token_expert_order", "expert_start_indices", "restore_token_order", "expert_ids",
+                "expert_usage_stats"):
+        assert torch.equal(fused[key].view(torch.int32), sep[key].view(torch.int32)), key
