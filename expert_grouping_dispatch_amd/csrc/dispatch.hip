@@ -246,7 +246,7 @@ struct LaunchMxfp4 {
   static hipError_t go(const u32x4* x, int64_t n_rows, int h16, int top_k,
                        const uint32_t* restore, uint8_t* q, uint8_t* scales, uint32_t limit,
                        hipStream_t s) {
-    const RowSplit rs = row_split(n_rows, h16 / 4, kMxThreads / 8);
+    const RowSplit rs = row_split(n_rows, h16 / 4, kMxThreads / 2);
     hipLaunchKernelGGL((k_dispatch_mxfp4<K, kEven, kPacked>), dim3(row_grid(n_rows * rs.split)),
                        dim3(kMxThreads), 0, s, x, n_rows, h16, top_k, restore, q, scales, limit, rs);
     return hipGetLastError();
