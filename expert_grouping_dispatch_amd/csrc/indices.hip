@@ -131,7 +131,7 @@ __device__ void wave_counts(const IdT* ids, IdT* wmap, int64_t n_slots, int64_t 
 template <bool kFromEnd>
 __device__ void wave_scatter(const WaveTile& tile, uint32_t n_experts, const uint32_t* off,
                              uint32_t* whist, uint32_t* __restrict__ teo,
-                             uint32_t* __restrict__ restore) {
+                             uint32_t* __restrict__ restore, int64_t n_slots) {
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
   const int nb = int(n_experts) + 1;
   for (int b = tid; b < nb; b += kIdxThreads) {
@@ -156,7 +156,9 @@ __device__ void wave_scatter(const WaveTile& tile, uint32_t n_experts, const uin
       const uint32_t i = uint32_t(tile.wbegin + r * kWave + lane);
       const bool routed = tile.key[r] < n_experts;
       restore[i] = routed ? pos : kSent;
-      teo[pos] = routed ? i : kSent;
+      // positions are < n_slots whenever the workspace was used as documented;
+      // the check keeps a misused one from writing out of bounds
+      if (int64_t(pos) < n_slots) teo[pos] = routed ? i : kSent;
     }
   }
 }
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
     __syncthreads();
     finalize_counts(hist, n_experts, base, esi, expert_ids, stats, soff, align);
     __syncthreads();
-    wave_scatter<false>(tile, n_experts, base, whist, teo, restore);
+    wave_scatter<false>(tile, n_experts, base, whist, teo, restore, n_slots);
     return;
   }
 
@@ -319,6 +321,10 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
   for (int b = tid; b < nb; b += kIdxThreads) hist[b] = 0;
   __syncthreads();
   const int64_t c = s_chunk;
+  if (c >= n_chunks) {  // only a workspace that was not zero-filled hands out such a ticket
+    if (tid == 0) atomicOr(ws.err, 2u);
+    return;
+  }
   chunk_histogram(ids, wmap, n_slots, c * kIdxChunk, n_experts, hist, pad_begin(pad, n_slots));
   __syncthreads();
 
@@ -379,7 +385,7 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scatter(
     if (b < nb) off[b] = offv[q];
   }
   __syncthreads();
-  wave_scatter<true>(tile, n_experts, off, lds + nb, teo, restore);
+  wave_scatter<true>(tile, n_experts, off, lds + nb, teo, restore, n_slots);
 }
 
 int64_t index_chunks(int64_t n_slots) {

@@ -136,8 +136,11 @@ size_t moe_create_indices_workspace_bytes(int64_t n_slots, int32_t n_experts);
  *                         that fit its size may follow).
  *                         Calls that share a workspace must not overlap.
  *                         Its first 32-bit word becomes nonzero (and stays
- *                         so) if a cross-workgroup wait ever gave up, which
- *                         a non-zeroed workspace can cause.
+ *                         so) if a cross-workgroup wait ever gave up or the
+ *                         call found the workspace not in the state a
+ *                         zero-filled one is left in; the outputs of such a
+ *                         call are unspecified, but every access stays
+ *                         inside the buffers passed.
  * All outputs are fully written, also when S = 0 or V = 0.
  */
 int moe_create_indices(const int32_t* topk_ids, int64_t n_slots, int32_t n_experts,

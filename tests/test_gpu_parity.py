@@ -498,3 +498,31 @@ def _launch_path(ids, w, real, e, x, y, st):
         o = torch.empty((n, h), dtype=torch.bfloat16, device=DEV)
         mod.moe_combine(y, d_w, idx["restore_token_order"], k, o)
     return dict(ids=d_ids, dispatch=out, q=q, scales=sc, combine=o, **idx)
+
+
+def test_workspace_not_zero_filled_sets_error_word():
+    """Misuse, forced from the host: the ticket word of the workspace is not
+    zero, so the first chunks are never handed out and later chunks wait for
+    them.  The waits are bounded; the call must finish, keep every write
+    inside the buffers (canaries after the outputs and the workspace stay
+    intact) and set the sticky error word.  The outputs are unspecified."""
+    n, k, e = 20000, 2, 16                      # 40000 slots, 20 chunks
+    s = n * k
+    ids = np.random.default_rng(5).integers(0, e, size=(n, k)).astype(np.int32)
+    d_ids = torch.from_numpy(ids).to(DEV)
+    pad = 4096
+    canary = 0x5A5A5A5A
+    teo = torch.full((s + pad,), canary, dtype=torch.int64, device=DEV).to(torch.int32).view(torch.uint32)
+    rest = torch.full((s + pad,), canary, dtype=torch.int64, device=DEV).to(torch.int32).view(torch.uint32)
+    esi = torch.empty(e + 1, dtype=torch.uint32, device=DEV)
+    eid = torch.empty(e, dtype=torch.int32, device=DEV)
+    stats = torch.empty(2, dtype=torch.uint32, device=DEV)
+    ws_bytes = mod.moe_create_indices_workspace_bytes(s, e)
+    ws = torch.zeros(ws_bytes + 65536, dtype=torch.uint8, device=DEV)
+    ws[ws_bytes:] = 0xA5
+    ws[:8].view(torch.int32)[1] = 3             # ticket word
+    mod.moe_create_indices(d_ids, e, teo[:s], esi, rest[:s], eid, stats, ws[:ws_bytes])
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32).item()) != 0
+    assert bool((teo[s:].view(torch.int32) == canary).all()) and bool((rest[s:].view(torch.int32) == canary).all())
+    assert bool((ws[ws_bytes:] == 0xA5).all())
