@@ -35,6 +35,11 @@ namespace {
 #ifndef MOE_MXFP4_NT_STORE
 #define MOE_MXFP4_NT_STORE 1
 #endif
+// Packed rows (17 bytes per block) are not 128-byte aligned, so adjacent
+// rows share cache lines; plain stores let the caches merge those lines.
+#ifndef MOE_MXFP4_PACKED_NT_STORE
+#define MOE_MXFP4_PACKED_NT_STORE 0
+#endif
 constexpr int kLoadsInFlight = MOE_DISPATCH_LOADS;  // 16-byte vectors each lane loads before storing
 constexpr int kDispatchThreads = MOE_DISPATCH_THREADS;
 constexpr int kMxThreads = MOE_MXFP4_THREADS;
@@ -200,7 +205,7 @@ __global__ __launch_bounds__(kMxThreads) void k_dispatch_mxfp4(
         const int64_t p = p32;
         if constexpr (kPacked) {
           uint8_t* row = q + p * (int64_t(nblk) * 17);  // 16 payload bytes + 1 scale byte per block
-          store_vec<MOE_MXFP4_NT_STORE>(reinterpret_cast<u32x4*>(row) + b, pv);
+          store_vec<MOE_MXFP4_PACKED_NT_STORE>(reinterpret_cast<u32x4*>(row) + b, pv);
           row[int64_t(nblk) * 16 + b] = sbyte;
         } else {
           store_vec<MOE_MXFP4_NT_STORE>(reinterpret_cast<u32x4*>(q) + p * nblk + b, pv);
