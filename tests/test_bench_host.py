@@ -1,0 +1,48 @@
+"""Host checks of bench.py's accounting (no GPU).
+
+The algorithmic bytes per pipeline are pinned to totals worked out by hand
+from the byte model (x read once per real token, only routed rows of the
+dispatch buffer and of y, index arrays read/written once) for each workload,
+so a slip in the per-stage formulas changes every GB/s figure and fails
+here."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# workload -> (routed slots V, bf16 pipeline bytes, MXFP4 pipeline bytes)
+EXPECTED = {
+    "tiny": (128, 199_760, 151_632),
+    "mixtral_prefill": (14_000, 354_212_624, 269_988_624),
+    "deepseek_v3_prefill": (32_768, 1_057_753_104, 712_771_600),
+    "decode": (776, 27_356_208, 19_186_480),
+    "large_prefill_stress": (491_520, 15_925_643_280, 10_750_920_720),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EXPECTED))
+def test_pipeline_bytes(name):
+    v, bf16, mx = EXPECTED[name]
+    w = workloads.BY_NAME[name]
+    b = bench.stage_bytes(w, v)
+    assert b["mask"] + b["indices"] + b["dispatch_bf16"] + b["combine"] == bf16
+    assert b["mask"] + b["indices"] + b["dispatch_mxfp4"] + b["combine"] == mx
+
+
+def test_routed_slots_of_the_workloads():
+    """V = real tokens x top_k for every workload (padding rows only are unrouted)."""
+    for name, (v, _, _) in EXPECTED.items():
+        w = workloads.BY_NAME[name]
+        assert w.real_tokens * w.top_k == v
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
