@@ -17,6 +17,9 @@
 // later call of any shape finds no published word it did not write.
 // Bucket b < E is expert b; bucket E collects the unrouted slots, which land
 // after every routed slot and fill token_expert_order[V, S) with sentinels.
+// For the one-call mask + index entry point, k_index_hist (or the single
+// workgroup) also counts the slots of padding rows as unrouted and writes -1
+// into them, so k_index_scatter reads the masked map.
 #include "common.h"
 #include "internal.h"
 
