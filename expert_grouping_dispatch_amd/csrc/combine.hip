@@ -1,10 +1,11 @@
 // Stage 4: combine ("Struct_ep_combine_wait": weighted sum of the routed
 // expert outputs of each token with its router weights).
 //
-// One workgroup per token; each lane owns 8 consecutive hidden elements (one
-// 16-byte vector) at a time, loads that vector from up to kBatch expert rows
-// at once, and accumulates in fp32 in ascending j.  Products and sums are
-// rounded separately (__fmul_rn / __fadd_rn, and the library is built with
+// One workgroup per token (per part of the row when there are few rows);
+// each lane owns 8 consecutive hidden elements (one 16-byte vector) at a
+// time, loads that vector from up to kBatch expert rows at once, and
+// accumulates in fp32 in ascending j.  Products and sums are rounded
+// separately (__fmul_rn / __fadd_rn, and the library is built with
 // contraction off), so the result is the same bits as the sequential
 // definition.
 #include "common.h"

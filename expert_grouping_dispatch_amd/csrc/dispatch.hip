@@ -1,9 +1,9 @@
 // Stage 3: dispatch token rows into the expert-contiguous buffer, as bf16 or
 // as MXFP4 ("Struct_ep_dispatch_async_mxfp4": input_tokens [num_tokens,
 // hidden_size] go to the experts of topk_ids; FP4 quants travel with their
-// scales).  Token-major: one workgroup per token reads the row once and
-// writes it to each of its routed positions, so x is read once per token
-// instead of once per slot.
+// scales).  Token-major: one workgroup per token (per part of the row when
+// there are few rows) reads the row once and writes it to each of its routed
+// positions, so x is read once per token instead of once per slot.
 #include "common.h"
 #include "internal.h"
 #include "rows.h"
@@ -22,7 +22,8 @@ namespace {
 #define MOE_MXFP4_THREADS 256
 #endif
 // Cache policy (measured on MI355X: plain loads and stores for the bf16 row
-// fan-out, plain loads and non-temporal stores for the MXFP4 rows).
+// fan-out, plain loads and non-temporal stores for the separate MXFP4 payload
+// rows, which are 128-byte aligned).
 #ifndef MOE_DISPATCH_NT_LOAD
 #define MOE_DISPATCH_NT_LOAD 0
 #endif
