@@ -53,15 +53,19 @@ def stage_bytes(w: workloads.Workload, n_routed: int) -> dict:
 
 
 def source_digest(kernel: str) -> str:
-    """Digest of the sources a kernel is built from (to tell stale counters)."""
+    """Digest of the code a kernel is built from (to tell stale counters):
+    its sources with comments and whitespace removed, so that only a change
+    of code, not of its comments, marks the counters as stale."""
     csrc = os.path.join(ROOT, "expert_grouping_dispatch_amd", "csrc")
     files = {"k_combine": ["combine.hip", "rows.h", "common.h"],
              "k_dispatch_bf16": ["dispatch.hip", "rows.h", "common.h"],
              "k_dispatch_mxfp4": ["dispatch.hip", "rows.h", "common.h"]}.get(kernel, [])
     hsh = hashlib.sha256()
     for f in files:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            hsh.update(fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            code = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        hsh.update("".join(code.split()).encode())
     return hsh.hexdigest()[:16]
 
 

@@ -46,3 +46,20 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_source_digest_ignores_comments(tmp_path, monkeypatch):
+    """Counters stay valid across comment edits and go stale on a code edit."""
+    import shutil
+    csrc = tmp_path / "expert_grouping_dispatch_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    real = os.path.join(ROOT, "expert_grouping_dispatch_amd", "csrc")
+    for f in ("combine.hip", "rows.h", "common.h"):
+        shutil.copy(os.path.join(real, f), csrc / f)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    d0 = bench.source_digest("k_combine")
+    text = (csrc / "combine.hip").read_text()
+    (csrc / "combine.hip").write_text("// a new comment\n" + text.replace("\n", "\n  ", 3))
+    assert bench.source_digest("k_combine") == d0
+    (csrc / "combine.hip").write_text(text.replace("kBatch = 8", "kBatch = 4"))
+    assert bench.source_digest("k_combine") != d0
