@@ -304,10 +304,12 @@ def test_argument_errors_on_device():
     assert e.value.status == 1
 
 
-def test_graph_replay_with_device_count():
-    """Capture mask+indices+dispatch+combine once; change only the device-side
-    count between replays (with eager work in between) and check each replay."""
-    n, k, e, h = 2048, 4, 64, 64
+@pytest.mark.parametrize("fused, n, k", [(False, 2048, 4), (True, 2048, 4), (False, 256, 8), (True, 256, 8)])
+def test_graph_replay_with_device_count(fused, n, k):
+    """Capture mask+indices+dispatch+combine once (mask and indices as two
+    calls, or as the one-call entry point); change only the device-side count
+    between replays (with eager work in between) and check each replay."""
+    e, h = 64, 64
     ids0, w, _, x, y = _rand_case(50, n, k, e, h, "distinct")
     d_ids = torch.from_numpy(ids0).to(DEV)
     d_src = d_ids.clone()
@@ -319,10 +321,15 @@ def test_graph_replay_with_device_count():
     comb = torch.empty((n, h), dtype=torch.bfloat16, device=DEV)
 
     def step():
-        mod.moe_mask_padding(d_ids, cnt, 0)
-        mod.moe_create_indices(d_ids, e, idx["token_expert_order"], idx["expert_start_indices"],
-                               idx["restore_token_order"], idx["expert_ids"], idx["expert_usage_stats"],
-                               idx["workspace"])
+        if fused:
+            mod.moe_mask_create_indices(d_ids, cnt, 0, e, idx["token_expert_order"], idx["expert_start_indices"],
+                                        idx["restore_token_order"], idx["expert_ids"], idx["expert_usage_stats"],
+                                        idx["workspace"])
+        else:
+            mod.moe_mask_padding(d_ids, cnt, 0)
+            mod.moe_create_indices(d_ids, e, idx["token_expert_order"], idx["expert_start_indices"],
+                                   idx["restore_token_order"], idx["expert_ids"], idx["expert_usage_stats"],
+                                   idx["workspace"])
         mod.moe_dispatch(x, k, idx["restore_token_order"], disp)
         mod.moe_dispatch_mxfp4(x, k, idx["restore_token_order"], q, sc)
         mod.moe_combine(y, d_w, idx["restore_token_order"], k, comb)
@@ -337,7 +344,7 @@ def test_graph_replay_with_device_count():
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         step()
-    for real in (1500, 7, 2048, 0, 1999):
+    for real in (n * 3 // 4, 7, n, 0, n - 49):
         d_ids.copy_(d_src)  # the mask works in place; restore the unmasked map eagerly
         cnt.fill_(real)
         torch.cuda.synchronize()
