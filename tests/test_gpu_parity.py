@@ -253,8 +253,12 @@ def test_combine_no_fma_and_fixed_order():
     np.testing.assert_array_equal(got, want)
 
 
-def test_positions_outside_buffer_are_skipped():
-    n, k, e, h = 50, 2, 4, 32
+@pytest.mark.parametrize("h", [32, 2048])
+def test_positions_outside_buffer_are_skipped(h):
+    """Output (dispatch) and input (combine) buffers shorter than the routed
+    rows: positions past them are skipped.  h = 2048 also cuts rows across
+    workgroups."""
+    n, k, e = 50, 2, 4
     ids, w, real, x, y = _rand_case(30, n, k, e, h)
     ref = oracle.create_indices(ids, e)
     restore = torch.from_numpy(ref["restore_token_order"].view(np.int32)).to(DEV).view(torch.uint32)
@@ -263,6 +267,12 @@ def test_positions_outside_buffer_are_skipped():
     mod.moe_dispatch(x, k, restore, out)
     want = oracle.dispatch(u16(x), ref["token_expert_order"], k, ref["n_routed"])[:limit]
     np.testing.assert_array_equal(u16(out), want)
+    q = torch.zeros((limit, h // 2), dtype=torch.uint8, device=DEV)
+    sc = torch.zeros((limit, h // 32), dtype=torch.uint8, device=DEV)
+    mod.moe_dispatch_mxfp4(x, k, restore, q, sc)
+    wq, wsc = oracle.dispatch_mxfp4(u16(x), ref["token_expert_order"], k, ref["n_routed"])
+    np.testing.assert_array_equal(q.cpu().numpy(), wq[:limit])
+    np.testing.assert_array_equal(sc.cpu().numpy(), wsc[:limit])
     comb = torch.empty((n, h), dtype=torch.bfloat16, device=DEV)
     mod.moe_combine(y[:limit], torch.from_numpy(w).to(DEV), restore, k, comb)
     r2 = ref["restore_token_order"].copy()
