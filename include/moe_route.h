@@ -8,6 +8,7 @@
  *   3. moe_dispatch         -- token rows copied into an expert-contiguous
  *      moe_dispatch_mxfp4      buffer, as bf16 or as MXFP4
  *   4. moe_combine          -- weighted sum of expert outputs back per token
+ * plus moe_mask_create_indices, stages 1 and 2 in one call.
  *
  * Conventions shared by every entry point
  *   - Pointers marked [device] are device (HBM) pointers on the current HIP
@@ -16,10 +17,14 @@
  *     keeps no pointer after a call returns.
  *   - Tensors are dense and row-major.  bf16 values are passed as their
  *     16-bit patterns (uint16_t).
- *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
- *     enqueued asynchronously; no call synchronises with the host or reads
- *     device data on the host, so a whole sequence can be captured into a
- *     HIP graph.
+ *   - `stream` is a hipStream_t of the current device (NULL = the legacy
+ *     default stream); the device check looks at the current device.  Work
+ *     is enqueued asynchronously; no call synchronises with the host or
+ *     reads device data on the host, so a whole sequence can be captured
+ *     into a HIP graph.
+ *   - Calls keep no state between them outside the buffers passed, so calls
+ *     on different streams may run at once, except that calls sharing an
+ *     index workspace must not overlap.
  *   - A slot is the pair (token t, choice j) with flat index i = t*top_k + j.
  *     MOE_SENTINEL (0xFFFFFFFF) marks "no slot / no position".
  *   - Return value: MOE_OK, or an error code with nothing enqueued.  Errors
