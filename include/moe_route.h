@@ -30,7 +30,10 @@
  *   - Return value: MOE_OK, or an error code with nothing enqueued.  Errors
  *     are argument errors detected on the host (null or misaligned pointer,
  *     size out of range), an undersized workspace, a device that is not
- *     gfx950 (rejected, never emulated), or a failed launch.  Bad *data*
+ *     gfx950 (rejected, never emulated), or a failed launch.  For tests of
+ *     that rejection, the environment variable MOE_ROUTE_ASSUME_ARCH, when
+ *     set, stands in for the device's architecture name (read once per
+ *     device and process).  Bad *data*
  *     (an expert id outside [0, n_experts), a position outside the output
  *     buffer) is not an error: such a slot is treated as unrouted.
  */

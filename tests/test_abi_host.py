@@ -119,3 +119,27 @@ def test_invalid_arguments_rejected_on_host():
     E = L.moe_combine_epilogue
     assert E(fake, 20, fake, fake, 10, 16, 2, ctypes.c_float(1.0), P(264), fake, None) == 1  # residual misaligned
     assert E(fake, 20, fake, fake, 10, 16, 2, ctypes.c_float(1.0), P(256 + 160), P(256), None) == 1  # overlap
+
+
+def _hip_device_count():
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return 0
+    n = ctypes.c_int(0)
+    return n.value if hip.hipGetDeviceCount(ctypes.byref(n)) == 0 else 0
+
+
+@pytest.mark.skipif(_hip_device_count() > 0, reason="a HIP device is present: valid arguments would launch")
+def test_no_device_is_rejected_after_the_argument_checks():
+    """Valid arguments with no HIP device: the device check returns
+    MOE_ERR_UNSUPPORTED_DEVICE and nothing is launched (the pointers are
+    never dereferenced)."""
+    L = mod.lib
+    fake, cnt = P(256), P(512)
+    assert L.moe_mask_padding(fake, 4, 2, cnt, 0, None) == 3
+    ws = mod.moe_create_indices_workspace_bytes(100, 8)
+    assert L.moe_create_indices(fake, 100, 8, fake, fake, fake, fake, fake, None, 0, P(1024), ws, None) == 3
+    assert L.moe_dispatch(fake, 10, 16, 2, fake, fake, 20, None) == 3
+    assert L.moe_dispatch_mxfp4(fake, 10, 64, 2, fake, fake, fake, 20, 0, None) == 3
+    assert L.moe_combine(fake, 20, fake, fake, 10, 16, 2, fake, None) == 3

@@ -543,3 +543,45 @@ def test_workspace_not_zero_filled_sets_error_word():
     assert int(ws[:4].view(torch.int32).item()) != 0
     assert bool((teo[s:].view(torch.int32) == canary).all()) and bool((rest[s:].view(torch.int32) == canary).all())
     assert bool((ws[ws_bytes:] == 0xA5).all())
+
+
+_ARCH_PROBE = r"""
+import sys, torch
+sys.path.insert(0, {root!r})
+import expert_grouping_dispatch_amd as mod
+ids = torch.arange(32, dtype=torch.int32, device="cuda").reshape(8, 4) % 5
+before = ids.clone()
+cnt = torch.tensor([3], dtype=torch.int32, device="cuda")
+codes = []
+try:
+    mod.moe_mask_padding(ids, cnt, 0)
+    codes.append(0)
+except mod.MoeError as exc:
+    codes.append(exc.status)
+idx = mod.alloc_indices(32, 5, "cuda")
+try:
+    mod.moe_create_indices(ids, 5, idx["token_expert_order"], idx["expert_start_indices"],
+                           idx["restore_token_order"], idx["expert_ids"], idx["expert_usage_stats"], idx["workspace"])
+    codes.append(0)
+except mod.MoeError as exc:
+    codes.append(exc.status)
+torch.cuda.synchronize()
+print("codes", codes, "unchanged", bool(torch.equal(ids, before)))
+"""
+
+
+@pytest.mark.parametrize("arch, want", [("gfx942", "codes [3, 3] unchanged True"),
+                                        ("gfx950:sramecc+:xnack-", "codes [0, 0] unchanged False")])
+def test_device_architecture_check(arch, want):
+    """A device that is not gfx950 is rejected before anything is launched;
+    the architecture name is stood in for through MOE_ROUTE_ASSUME_ARCH, in a
+    fresh process (the check is made once per device and process)."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, MOE_ROUTE_ASSUME_ARCH=arch)
+    r = subprocess.run([sys.executable, "-c", _ARCH_PROBE.format(root=root)], env=env, capture_output=True,
+                       text=True, timeout=180)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert want in r.stdout, r.stdout
