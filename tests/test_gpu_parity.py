@@ -585,3 +585,22 @@ def test_device_architecture_check(arch, want):
                        text=True, timeout=180)
     assert r.returncode == 0, r.stderr[-2000:]
     assert want in r.stdout, r.stdout
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes(seed):
+    """Seeded random shapes through the whole path, element by element against
+    the oracle: row counts across the one-workgroup / multi-chunk boundary and
+    the split-row range, every top_k path, expert counts, hidden sizes (some
+    not a multiple of 32: bf16 only), counts outside [0, N] and garbage ids."""
+    g = np.random.default_rng(9000 + seed)
+    k = int(g.choice([1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 16, 33]))
+    n = int(g.integers(1, max(2, 24000 // k)))
+    e = int(g.choice([1, 2, 7, 8, 64, 255, 256, 300, 1024]))
+    h = int(g.choice([8, 24, 32, 96, 256, 1000, 2048, 4096]))
+    kind = str(g.choice(["uniform", "garbage", "distinct" if k <= e else "uniform", "half_empty"]))
+    real = int(g.choice([n, n - 1, 0, n // 2, n + 3, -5]))
+    ids, w, _, x, y = _rand_case(9000 + seed, n, k, e, h, kind)
+    variants = ("bf16",) if h % 32 else ("bf16", "mxfp4")
+    print(f"[parity] random seed={seed}: n={n} k={k} e={e} h={h} kind={kind} real={real}", flush=True)
+    _full_check(ids, w, real, e, x, y, variants)
