@@ -272,8 +272,10 @@ def copy_ceiling(torch, gib: float = 2.0, reps: int = 10) -> float:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 20 on the stress workload, 200 on the mid-size ones, "
+                         "1000 on the latency-bound tiny and decode workloads)")
+    ap.add_argument("--warmup", type=int, default=None, help="warm-up steps (default: 3, or 10 below stress size)")
     ap.add_argument("--workload", default="large_prefill_stress", choices=sorted(workloads.BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
@@ -299,6 +301,10 @@ def main():
 
     cfg = [w.name for w in workloads.WORKLOADS].index(args.workload)
     w = workloads.WORKLOADS[cfg]
+    if args.steps is None:
+        args.steps = {"large_prefill_stress": 20, "tiny": 1000, "decode": 1000}.get(w.name, 200)
+    if args.warmup is None:
+        args.warmup = 3 if w.name == "large_prefill_stress" else 10
     n, k, h, e = w.n_rows, w.top_k, w.hidden, w.n_experts
     s = n * k
     dev = torch.device("cuda", 0)
