@@ -225,9 +225,10 @@ int moe_dispatch(const uint16_t* input_tokens, int64_t n_rows, int32_t hidden, i
  * position the row's slots map to:
  *   scale exponent  se = clamp(floor(log2(max |x|)) - 2, -127, 127),
  *                   se = -127 for an all-zero block; stored as se + 127.
- *                   With MOE_MXFP4_EVEN_SCALE (the page's "per-token
- *                   even-mode scales", read as: round max |x| to E2M1's one
- *                   mantissa bit, halves up, before the floor):
+ *                   With MOE_MXFP4_EVEN_SCALE (the page names per-token
+ *                   even-mode scales without defining them; read here as:
+ *                   round max |x| to E2M1's one mantissa bit, halves up,
+ *                   before the floor):
  *                   floor(log2(max |x|)) gains 1 when the mantissa fraction
  *                   of max |x| is >= 0.75, so a block maximum that would
  *                   scale into [7, 8) lands in [3.5, 4) instead.
@@ -242,7 +243,7 @@ int moe_dispatch(const uint16_t* input_tokens, int64_t n_rows, int32_t hidden, i
  *   out_q         [device] uint8 [out_rows, hidden/2], 16-byte aligned; with
  *                 MOE_MXFP4_PACKED_ROWS uint8 [out_rows, hidden/2 + hidden/32]
  *                 holding each slot's payload followed by its scale bytes
- *                 (the page's scales "packed alongside the FP4 quants").
+ *                 (the page has the scales travel with the FP4 quants).
  *   out_scales    [device] uint8 [out_rows, hidden/32]; NULL with
  *                 MOE_MXFP4_PACKED_ROWS.
  *   flags         0, or an OR of MOE_MXFP4_EVEN_SCALE and MOE_MXFP4_PACKED_ROWS.
