@@ -27,7 +27,8 @@ constexpr int64_t kIdxChunk = int64_t(kIdxThreads) * kIdxRounds;
 // the next call of any shape: the last ticket holder resets the ticket, and
 // the scatter kernel zeroes every lookback word of the call after reading it.
 struct IndexWorkspace {
-  uint32_t* err;        // [1]  nonzero once a cross-workgroup wait gave up (sticky)
+  uint32_t* err;        // [1]  sticky: bit 0 a cross-workgroup wait gave up, bit 1 a
+                        //      ticket past the last chunk (workspace not zero-filled)
   uint32_t* ticket;     // [1]  chunk ticket counter
   uint32_t* base;       // [E+1]         first position of bucket b
   uint64_t* flags;      // [chunks][E+1] (status << 32 | count) lookback words
