@@ -523,7 +523,7 @@ def test_workspace_not_zero_filled_sets_error_word():
     them.  The waits are bounded; the call must finish, keep every write
     inside the buffers (canaries after the outputs and the workspace stay
     intact) and set the sticky error word.  The outputs are unspecified."""
-    n, k, e = 20000, 2, 16                      # 40000 slots, 20 chunks
+    n, k, e = 100000, 2, 16                     # 200000 slots: the many-workgroup path
     s = n * k
     ids = np.random.default_rng(5).integers(0, e, size=(n, k)).astype(np.int32)
     d_ids = torch.from_numpy(ids).to(DEV)
