@@ -107,6 +107,50 @@ def test_workload_full_size_sampled(cfg):
         assert int(res["combine"][real:].view(torch.int16).abs().max()) == 0
 
 
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_workload_full_size_every_row(cfg):
+    """Full-size workloads, every routed row, against definitions evaluated on
+    the GPU with plain torch operations (the positions come from the oracle):
+    bf16 dispatch row p is x[teo[p] // k]; the MXFP4 bytes of all k copies of
+    a token are identical (the rows themselves are pinned to the oracle on
+    samples); combine equals fp32 products and sums, each rounded on its own,
+    j ascending, unrouted j skipped, then bf16 round-to-nearest-even."""
+    w = workloads.WORKLOADS[cfg]
+    ids, wts, real = workloads.make_routing(w, cfg)
+    x, y = workloads.make_dense(w, cfg, DEV)
+    res = run_path(mod, ids, real, w.n_experts, x, y, wts, ("bf16", "mxfp4"))
+    _, ref = _oracle_front(ids, real, w.n_experts)
+    n, k, v = w.n_rows, w.top_k, ref["n_routed"]
+    teo = torch.from_numpy(ref["token_expert_order"][:v].astype(np.int64)).to(DEV)
+    rest = torch.from_numpy(ref["restore_token_order"].astype(np.int64)).to(DEV).view(n, k)
+    block = 4096
+    for p0 in range(0, v, block * 8):
+        sl = slice(p0, min(v, p0 + block * 8))
+        assert torch.equal(res["dispatch"][sl].view(torch.int16), x[teo[sl] // k].view(torch.int16)), p0
+    sent = torch.tensor(SENT, dtype=torch.int64, device=DEV)
+    routed = rest != sent
+    for t0 in range(0, real, block):
+        t1 = min(real, t0 + block)
+        r = rest[t0:t1]
+        first = r[:, 0]
+        for j in range(1, k):
+            ok = routed[t0:t1, j] & routed[t0:t1, 0]
+            a, b = r[:, j][ok], first[ok]
+            assert torch.equal(res["q"][a], res["q"][b]) and torch.equal(res["scales"][a], res["scales"][b])
+    wt = torch.from_numpy(wts).to(DEV)
+    for t0 in range(0, n, block):
+        t1 = min(n, t0 + block)
+        acc = torch.zeros((t1 - t0, w.hidden), dtype=torch.float32, device=DEV)
+        for j in range(k):
+            rj = rest[t0:t1, j]
+            ok = rj != sent
+            yj = y[torch.where(ok, rj, torch.zeros_like(rj))].float()
+            prod = wt[t0:t1, j:j + 1] * yj
+            acc = torch.where(ok[:, None], acc + prod, acc)
+        want = acc.to(torch.bfloat16).view(torch.int16)
+        assert torch.equal(res["combine"][t0:t1].view(torch.int16), want), t0
+
+
 # ---------------------------------------------------------------- edge cases
 def _rand_case(seed, n, k, e, h, kind="uniform", real=None):
     g = np.random.default_rng(seed)
