@@ -417,10 +417,12 @@ def test_graph_replay_with_device_count(fused, n, k):
         _check_combine(u16(comb), oracle.combine(u16(y), w, ref["restore_token_order"], k))
 
 
-def test_indices_beyond_int32_slots():
-    """2^31 + 4099 slots (past the int32 range, ragged last chunk), E = 1024:
-    every property that defines the outputs, checked on the GPU in pieces."""
-    S, E = (1 << 31) + 4099, 1024
+@pytest.mark.parametrize("S, E", [((1 << 31) + 4099, 1024), (0xFFFFFFFE, 256)])
+def test_indices_beyond_int32_slots(S, E):
+    """Past the int32 range (2^31 + 4099 slots, ragged last chunk, E = 1024)
+    and at the largest slot count the sentinel allows (2^32 - 2, positions up
+    to 2^32 - 3): every property that defines the outputs, checked on the GPU
+    in pieces."""
     print(f"[parity] create_indices at S={S} E={E}", flush=True)
     gen = torch.Generator(device=DEV)
     gen.manual_seed(20261203)
