@@ -1,9 +1,10 @@
 // Stage 2: expert-grouped indices ("moe_create_indices": histogram the expert
 // ids, scan the histogram into CSR offsets, scatter the slots).
 //
-// The pages' kernel is one CTA.  Here the slots are cut into chunks of
-// kIdxChunk; for S <= kIdxChunk one workgroup still does all three steps in
-// one launch, otherwise:
+// The pages' kernel is one CTA.  Here the slots are cut into chunks (of
+// kIdxChunk slots, or half that for inputs up to kIdxSmallMaxSlots so that
+// more workgroups share them); for S <= kIdxChunk one workgroup still does
+// all three steps in one launch, otherwise:
 //   k_index_hist     per chunk (taken by ticket): LDS histogram, then a
 //                    decoupled lookback over earlier chunks gives, per
 //                    bucket, the number of slots in all earlier chunks; the
@@ -74,53 +75,54 @@ __device__ __forceinline__ uint32_t slot_key(const IdT* ids, IdT* wmap, int64_t 
 
 // Count the chunk's slots per bucket into hist[0..E] (LDS, zeroed by caller).
 // Only totals are needed here, so plain LDS atomics do.
-template <typename IdT>
+template <int R, typename IdT>
 __device__ void chunk_histogram(const IdT* ids, IdT* wmap, int64_t n_slots, int64_t begin,
                                 uint32_t n_experts, uint32_t* hist, int64_t pad_from) {
   const int tid = threadIdx.x;
-  uint32_t key[kIdxRounds];
-  bool valid[kIdxRounds];
+  uint32_t key[R];
+  bool valid[R];
 #pragma unroll
-  for (int r = 0; r < kIdxRounds; ++r) {
+  for (int r = 0; r < R; ++r) {
     const int64_t i = begin + int64_t(r) * kIdxThreads + tid;
     valid[r] = i < n_slots;
     key[r] = valid[r] ? slot_key(ids, wmap, i, pad_from, n_experts) : 0u;
   }
 #pragma unroll
-  for (int r = 0; r < kIdxRounds; ++r)
+  for (int r = 0; r < R; ++r)
     if (valid[r]) atomicAdd(&hist[key[r]], 1u);
 }
 
-// One wave's slots of a chunk: wave w owns the kIdxRounds*64 consecutive
-// slots starting at begin + w*kIdxRounds*64, so (wave, round, lane) order is
+// One wave's slots of a chunk of R rounds: wave w owns the R*64 consecutive
+// slots starting at begin + w*R*64, so (wave, round, lane) order is
 // ascending slot index.  Keys and peer masks stay in registers between the
 // counting pass and the scatter pass.
+template <int R>
 struct WaveTile {
-  uint32_t key[kIdxRounds];
-  bool valid[kIdxRounds];
-  uint64_t peers[kIdxRounds];
+  uint32_t key[R];
+  bool valid[R];
+  uint64_t peers[R];
   int64_t wbegin;
 };
 
 // Load the wave's keys and count them per bucket into its own LDS row
 // whist[wave][0..E] (only this wave touches the row; no atomics).
-template <typename IdT>
+template <int R, typename IdT>
 __device__ void wave_counts(const IdT* ids, IdT* wmap, int64_t n_slots, int64_t begin,
-                            uint32_t n_experts, int nbits, uint32_t* whist, WaveTile& tile,
+                            uint32_t n_experts, int nbits, uint32_t* whist, WaveTile<R>& tile,
                             int64_t pad_from) {
   const int lane = __lane_id(), wave = threadIdx.x / kWave;
   const int nb = int(n_experts) + 1;
   uint32_t* my = whist + wave * nb;
-  tile.wbegin = begin + int64_t(wave) * kIdxRounds * kWave;
+  tile.wbegin = begin + int64_t(wave) * R * kWave;
 #pragma unroll
-  for (int r = 0; r < kIdxRounds; ++r) {
+  for (int r = 0; r < R; ++r) {
     const int64_t i = tile.wbegin + r * kWave + lane;
     tile.valid[r] = i < n_slots;
     tile.key[r] = tile.valid[r] ? slot_key(ids, wmap, i, pad_from, n_experts) : 0u;
   }
   for (int b = lane; b < nb; b += kWave) my[b] = 0;
 #pragma unroll
-  for (int r = 0; r < kIdxRounds; ++r) {
+  for (int r = 0; r < R; ++r) {
     tile.peers[r] = match_peers(tile.key[r], nbits, tile.valid[r]);
     if (tile.valid[r] && is_leader(tile.peers[r])) my[tile.key[r]] += uint32_t(__popcll(tile.peers[r]));
   }
@@ -131,8 +133,8 @@ __device__ void wave_counts(const IdT* ids, IdT* wmap, int64_t n_slots, int64_t 
 // past its last one.  Turns whist into per-wave running starts (exclusive
 // prefix over waves seeded with the chunk's start), then each slot's position
 // is its wave's running start plus its rank among lower peer lanes.
-template <bool kFromEnd>
-__device__ void wave_scatter(const WaveTile& tile, uint32_t n_experts, const uint32_t* off,
+template <bool kFromEnd, int R>
+__device__ void wave_scatter(const WaveTile<R>& tile, uint32_t n_experts, const uint32_t* off,
                              uint32_t* whist, uint32_t* __restrict__ teo,
                              uint32_t* __restrict__ restore, int64_t n_slots) {
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
@@ -151,7 +153,7 @@ __device__ void wave_scatter(const WaveTile& tile, uint32_t n_experts, const uin
   uint32_t* my = whist + wave * nb;
   const uint64_t below = lanes_below();
 #pragma unroll
-  for (int r = 0; r < kIdxRounds; ++r) {
+  for (int r = 0; r < R; ++r) {
     uint32_t pos = 0;
     if (tile.valid[r]) pos = my[tile.key[r]] + uint32_t(__popcll(tile.peers[r] & below));
     if (tile.valid[r] && is_leader(tile.peers[r])) my[tile.key[r]] += uint32_t(__popcll(tile.peers[r]));
@@ -283,10 +285,11 @@ __device__ uint32_t lookback(const uint64_t* flags, int64_t c, int nb, int b, ui
 
 }  // namespace
 
+// Chunks are R rounds of kIdxThreads slots.
 // n_chunks == 1: one workgroup does histogram, scan and scatter.
 // n_chunks > 1: histogram + lookback + (last ticket) CSR outputs; the
 // scatter follows in k_index_scatter.
-template <typename IdT>
+template <typename IdT, int R>
 __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
     const IdT* ids, int64_t n_slots, uint32_t n_experts, int nbits,
     int64_t n_chunks, IndexWorkspace ws, uint32_t* __restrict__ esi,
@@ -303,7 +306,7 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
     // one workgroup: count per wave, total the counts, scan, scatter
     uint32_t* base = lds + nb;
     uint32_t* whist = lds + 2 * nb;
-    WaveTile tile;
+    WaveTile<R> tile;
     wave_counts(ids, wmap, n_slots, 0, n_experts, nbits, whist, tile, pad_begin(pad, n_slots));
     __syncthreads();
     for (int b = tid; b < nb; b += kIdxThreads) {
@@ -328,7 +331,8 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
     if (tid == 0) atomicOr(ws.err, 2u);
     return;
   }
-  chunk_histogram(ids, wmap, n_slots, c * kIdxChunk, n_experts, hist, pad_begin(pad, n_slots));
+  chunk_histogram<R>(ids, wmap, n_slots, c * (int64_t(R) * kIdxThreads), n_experts, hist,
+                     pad_begin(pad, n_slots));
   __syncthreads();
 
   for (int b = tid; b < nb; b += kIdxThreads) {
@@ -353,7 +357,7 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
   }
 }
 
-template <typename IdT>
+template <typename IdT, int R>
 __global__ __launch_bounds__(kIdxThreads) void k_index_scatter(
     const IdT* __restrict__ ids, int64_t n_slots, uint32_t n_experts, int nbits,
     IndexWorkspace ws, uint32_t* __restrict__ teo, uint32_t* __restrict__ restore) {
@@ -378,10 +382,10 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scatter(
     const int b = threadIdx.x + q * kIdxThreads;
     if (b < nb) ws.flags[c * nb + b] = 0u;
   }
-  WaveTile tile;
+  WaveTile<R> tile;
   // the map was masked by k_index_hist, so it is read as it is now
-  wave_counts(ids, static_cast<IdT*>(nullptr), n_slots, c * kIdxChunk, n_experts, nbits, lds + nb,
-              tile, n_slots);
+  wave_counts(ids, static_cast<IdT*>(nullptr), n_slots, c * (int64_t(R) * kIdxThreads), n_experts,
+              nbits, lds + nb, tile, n_slots);
 #pragma unroll
   for (int q = 0; q < kMaxPerThread; ++q) {
     const int b = threadIdx.x + q * kIdxThreads;
@@ -391,8 +395,16 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scatter(
   wave_scatter<true>(tile, n_experts, off, lds + nb, teo, restore, n_slots);
 }
 
+// Rounds per chunk: up to kIdxChunk slots one workgroup takes them all; up to
+// kIdxSmallMaxSlots, chunks of kIdxSmallRounds rounds put more workgroups on
+// the few chunks there are; larger inputs use kIdxRounds.
+int index_rounds(int64_t n_slots) {
+  return (n_slots > kIdxChunk && n_slots <= kIdxSmallMaxSlots) ? kIdxSmallRounds : kIdxRounds;
+}
+
 int64_t index_chunks(int64_t n_slots) {
-  return n_slots <= kIdxChunk ? 1 : (n_slots + kIdxChunk - 1) / kIdxChunk;
+  const int64_t chunk = int64_t(kIdxThreads) * index_rounds(n_slots);
+  return n_slots <= kIdxChunk ? 1 : (n_slots + chunk - 1) / chunk;
 }
 
 // Fixed layout for every shape: header words, bucket starts for the largest
@@ -401,8 +413,15 @@ constexpr size_t kWsHeader = 256;
 constexpr size_t kWsBase = kWsHeader;
 constexpr size_t kWsFlags = kWsBase + ((size_t(MOE_MAX_BUCKETS) * 4 + 255) & ~size_t(255));
 
+// Sized for at least as many chunks as any smaller input uses, so that a
+// workspace sized for some n_slots also fits every smaller one.
 size_t index_workspace_bytes(int64_t n_slots, int n_experts) {
-  const size_t c = size_t(index_chunks(n_slots)), nb = size_t(n_experts) + 1;
+  int64_t chunks = index_chunks(n_slots);
+  if (n_slots > kIdxSmallMaxSlots) {
+    const int64_t small_most = kIdxSmallMaxSlots / (int64_t(kIdxThreads) * kIdxSmallRounds);
+    chunks = chunks > small_most ? chunks : small_most;
+  }
+  const size_t c = size_t(chunks), nb = size_t(n_experts) + 1;
   return kWsFlags + align256(c * nb * 8);
 }
 
@@ -418,6 +437,24 @@ IndexWorkspace index_workspace_carve(void* ws, int64_t n_slots, int n_experts) {
   return w;
 }
 
+// The two launches of the many-chunk path, chunks of R rounds.
+template <typename IdT, int R>
+hipError_t launch_chunks(const IdT* ids, int64_t n_slots, int n_experts, int nbits, int64_t chunks,
+                         IndexWorkspace ws, uint32_t* esi, int32_t* expert_ids, uint32_t* stats,
+                         uint32_t* soff, uint32_t align, uint32_t* teo, uint32_t* restore,
+                         PadMask pad, IdT* wmap, hipStream_t s) {
+  const int nb = n_experts + 1;
+  hipLaunchKernelGGL((k_index_hist<IdT, R>), dim3(uint32_t(chunks)), dim3(kIdxThreads),
+                     size_t(nb) * sizeof(uint32_t), s, ids, n_slots, uint32_t(n_experts), nbits,
+                     chunks, ws, esi, expert_ids, stats, soff, align, teo, restore, pad, wmap);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_index_scatter<IdT, R>), dim3(uint32_t(chunks)), dim3(kIdxThreads),
+                     size_t(1 + kIdxWaves) * nb * sizeof(uint32_t), s, ids, n_slots,
+                     uint32_t(n_experts), nbits, ws, teo, restore);
+  return hipGetLastError();
+}
+
 template <typename IdT>
 hipError_t launch_create_indices(const IdT* ids, int64_t n_slots, int n_experts, uint32_t* teo,
                                  uint32_t* esi, uint32_t* restore, int32_t* expert_ids,
@@ -431,20 +468,17 @@ hipError_t launch_create_indices(const IdT* ids, int64_t n_slots, int n_experts,
   IdT* wmap = pad.count != nullptr ? const_cast<IdT*>(ids) : nullptr;
   if (chunks == 1) {
     const size_t lds = size_t(2 + kIdxWaves) * nb * sizeof(uint32_t);
-    hipLaunchKernelGGL(k_index_hist<IdT>, dim3(1), dim3(kIdxThreads), lds, s, ids, n_slots,
-                       uint32_t(n_experts), nbits, chunks, ws, esi, expert_ids, stats, soff, align,
-                       teo, restore, pad, wmap);
+    hipLaunchKernelGGL((k_index_hist<IdT, kIdxRounds>), dim3(1), dim3(kIdxThreads), lds, s, ids,
+                       n_slots, uint32_t(n_experts), nbits, chunks, ws, esi, expert_ids, stats, soff,
+                       align, teo, restore, pad, wmap);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(k_index_hist<IdT>, dim3(uint32_t(chunks)), dim3(kIdxThreads),
-                     size_t(nb) * sizeof(uint32_t), s, ids, n_slots, uint32_t(n_experts), nbits,
-                     chunks, ws, esi, expert_ids, stats, soff, align, teo, restore, pad, wmap);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_index_scatter<IdT>, dim3(uint32_t(chunks)), dim3(kIdxThreads),
-                     size_t(1 + kIdxWaves) * nb * sizeof(uint32_t), s, ids, n_slots,
-                     uint32_t(n_experts), nbits, ws, teo, restore);
-  return hipGetLastError();
+  if (index_rounds(n_slots) == kIdxSmallRounds)
+    return launch_chunks<IdT, kIdxSmallRounds>(ids, n_slots, n_experts, nbits, chunks, ws, esi,
+                                               expert_ids, stats, soff, align, teo, restore, pad,
+                                               wmap, s);
+  return launch_chunks<IdT, kIdxRounds>(ids, n_slots, n_experts, nbits, chunks, ws, esi, expert_ids,
+                                        stats, soff, align, teo, restore, pad, wmap, s);
 }
 
 template hipError_t launch_create_indices<int32_t>(const int32_t*, int64_t, int, uint32_t*,

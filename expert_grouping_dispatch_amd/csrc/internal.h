@@ -17,9 +17,19 @@ namespace moe {
 #ifndef MOE_IDX_ROUNDS
 #define MOE_IDX_ROUNDS 4
 #endif
+// Inputs of (kIdxChunk, kIdxSmallMaxSlots] slots use chunks of
+// kIdxSmallRounds rounds instead, so that more workgroups share them.
+#ifndef MOE_IDX_SMALL_ROUNDS
+#define MOE_IDX_SMALL_ROUNDS 2
+#endif
+#ifndef MOE_IDX_SMALL_MAX_SLOTS
+#define MOE_IDX_SMALL_MAX_SLOTS 65536
+#endif
 constexpr int kIdxThreads = MOE_IDX_THREADS;
 constexpr int kIdxWaves = kIdxThreads / 64;
 constexpr int kIdxRounds = MOE_IDX_ROUNDS;
+constexpr int kIdxSmallRounds = MOE_IDX_SMALL_ROUNDS;
+constexpr int64_t kIdxSmallMaxSlots = MOE_IDX_SMALL_MAX_SLOTS;
 constexpr int64_t kIdxChunk = int64_t(kIdxThreads) * kIdxRounds;
 #define MOE_MAX_BUCKETS 1025  // experts + the unrouted bucket
 
@@ -34,6 +44,7 @@ struct IndexWorkspace {
   uint64_t* flags;      // [chunks][E+1] (status << 32 | count) lookback words
 };
 
+int index_rounds(int64_t n_slots);
 int64_t index_chunks(int64_t n_slots);
 size_t index_workspace_bytes(int64_t n_slots, int n_experts);
 IndexWorkspace index_workspace_carve(void* ws, int64_t n_slots, int n_experts);

@@ -143,3 +143,17 @@ def test_no_device_is_rejected_after_the_argument_checks():
     assert L.moe_dispatch(fake, 10, 16, 2, fake, fake, 20, None) == 3
     assert L.moe_dispatch_mxfp4(fake, 10, 64, 2, fake, fake, fake, 20, 0, None) == 3
     assert L.moe_combine(fake, 20, fake, fake, 10, 16, 2, fake, None) == 3
+
+
+def test_workspace_size_is_monotone_in_slots():
+    """A workspace sized for some slot count fits every smaller one (across the
+    switch between chunk sizes too)."""
+    f = mod.moe_create_indices_workspace_bytes
+    sizes = sorted(set(list(range(0, 140000, 97)) + [2047, 2048, 2049, 65535, 65536, 65537, 131072, 131073,
+                                                     524288, 2 ** 32 - 2]))
+    for e in (1, 8, 256, 1024):
+        prev = 0
+        for s in sizes:
+            b = f(s, e)
+            assert b >= prev, (s, e)
+            prev = b
