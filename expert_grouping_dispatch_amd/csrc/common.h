@@ -37,21 +37,38 @@ __device__ __forceinline__ void agent_store_u64(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Inclusive wave-wide prefix sum (Hillis-Steele over shuffles).
+// Wave-wide scans with DPP lane moves (register to register, no LDS).  A
+// wave64 is 4 rows of 16 lanes: row_shr:1/2/4/8 give each lane the scan over
+// its row (lanes with no source read 0), then row_bcast:15 adds row r-1's last
+// lane into rows 1 and 3, and row_bcast:31 adds lane 31 into rows 2 and 3.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), kCtrl, kRowMask, 0xF, false));
+}
+
+// Inclusive wave-wide prefix sum.
 __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const uint32_t o = __shfl_up(v, d, kWave);
-    if (lane >= d) v += o;
-  }
+  v += dpp<kDppRowShr1, 0xF>(v);
+  v += dpp<kDppRowShr2, 0xF>(v);
+  v += dpp<kDppRowShr4, 0xF>(v);
+  v += dpp<kDppRowShr8, 0xF>(v);
+  v += dpp<kDppRowBcast15, 0xA>(v);
+  v += dpp<kDppRowBcast31, 0xC>(v);
   return v;
 }
 
+// Largest value over the wave, returned to every lane.
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-#pragma unroll
-  for (int d = kWave / 2; d > 0; d >>= 1) v = max(v, (uint32_t)__shfl_xor(v, d, kWave));
-  return v;
+  v = max(v, dpp<kDppRowShr1, 0xF>(v));
+  v = max(v, dpp<kDppRowShr2, 0xF>(v));
+  v = max(v, dpp<kDppRowShr4, 0xF>(v));
+  v = max(v, dpp<kDppRowShr8, 0xF>(v));
+  v = max(v, dpp<kDppRowBcast15, 0xA>(v));
+  v = max(v, dpp<kDppRowBcast31, 0xC>(v));
+  return uint32_t(__builtin_amdgcn_readlane(int(v), kWave - 1));
 }
 
 }  // namespace moe
