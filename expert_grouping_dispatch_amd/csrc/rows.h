@@ -16,8 +16,8 @@ inline uint32_t row_grid(int64_t n_rows) {
   return uint32_t(n_rows < kMaxRowBlocks ? n_rows : kMaxRowBlocks);
 }
 
-// With few rows, one workgroup per row leaves most CUs idle and each
-// workgroup moves a whole row alone.  Then each row is cut into `split` parts
+// Combine: with few rows, one workgroup per row leaves most CUs idle and
+// each workgroup moves a whole row alone.  Then each row is cut into `split` parts
 // of `len` units (16-byte vectors, or MXFP4 blocks), one workgroup per part,
 // aiming at about kRowSplitTarget workgroups and parts of at least
 // `min_len` units.  Large inputs keep split = 1.
@@ -35,6 +35,12 @@ inline RowSplit row_split(int64_t n_rows, int units, int min_len) {
     if (split < 1) split = 1;
   }
   return RowSplit{split, (units + split - 1) / split};
+}
+
+// Dispatch workgroups take `lanes` consecutive units of a row (one per
+// lane), so a row is cut into ceil(units / lanes) parts whatever the row count.
+inline int part_count(int units, int lanes) {
+  return units > lanes ? (units + lanes - 1) / lanes : 1;
 }
 
 // Positions >= limit are skipped; limit <= 0xFFFFFFFF so the sentinel is

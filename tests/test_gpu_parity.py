@@ -481,6 +481,24 @@ def test_indices_beyond_int32_slots(S, E):
     assert n_unrouted == S - v
 
 
+def test_dispatch_rows_beyond_one_item_grid():
+    """More (token, part) items than a one-workgroup-per-item bf16 grid takes
+    (2^25 + 37 rows of 8 elements, top_k = 1): the workgroups loop over
+    tokens.  Every routed row against the oracle."""
+    n, k, h, e = (1 << 25) + 37, 1, 8, 64
+    print(f"[parity] dispatch bf16 with n={n} k={k} h={h}", flush=True)
+    g = np.random.default_rng(4242)
+    ids = g.integers(-1, e, size=(n, k), dtype=np.int32)
+    ref = oracle.create_indices(ids, e)
+    v = ref["n_routed"]
+    xb = g.integers(0, 1 << 16, size=(n, h), dtype=np.uint16)
+    x = bf16_from_bits(xb, DEV)
+    restore = torch.from_numpy(ref["restore_token_order"].view(np.int32)).to(DEV).view(torch.uint32)
+    out = torch.zeros((n * k, h), dtype=torch.bfloat16, device=DEV)
+    mod.moe_dispatch(x, k, restore, out)
+    np.testing.assert_array_equal(u16(out[:v]), oracle.dispatch(xb, ref["token_expert_order"], k, v))
+
+
 def test_workspace_reuse_across_shapes():
     """One zero-filled workspace serves calls of different sizes, expert
     counts and id widths in any order: nothing an earlier call left in it is
