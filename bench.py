@@ -29,8 +29,21 @@ import workloads  # noqa: E402
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, AMD published peak
 METRIC = "routed token-slots/s + achieved HBM GB/s vs peak (index+dispatch+combine)"
 STAGES = ("mask", "indices", "dispatch_bf16", "dispatch_mxfp4", "combine")
-KERNEL_OF_STAGE = {"dispatch_bf16": "k_dispatch_bf16", "dispatch_mxfp4": "k_dispatch_mxfp4",
-                   "combine": "k_combine"}
+ROW_STAGES = ("dispatch_bf16", "dispatch_mxfp4", "combine")
+
+
+def kernel_of_stage(stage: str, w) -> str:
+    """Name of the kernel the library launches for a row stage on workload w
+    (a label for the roofline line and the profile it is checked against).
+    top_k <= 8 takes the loop-free bf16 dispatch; combine takes it too when
+    the routed rows of y are under 1 GiB, whole-row workgroups otherwise."""
+    if stage == "dispatch_mxfp4":
+        return "k_dispatch_mxfp4"
+    if w.top_k > 8:
+        return "k_dispatch_bf16" if stage == "dispatch_bf16" else "k_combine"
+    if stage == "dispatch_bf16":
+        return "k_dispatch_bf16_parts"
+    return "k_combine_parts" if w.n_rows * w.top_k * w.hidden * 2 < (1 << 30) else "k_combine"
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -57,9 +70,8 @@ def source_digest(kernel: str) -> str:
     its sources with comments and whitespace removed, so that only a change
     of code, not of its comments, marks the counters as stale."""
     csrc = os.path.join(ROOT, "expert_grouping_dispatch_amd", "csrc")
-    files = {"k_combine": ["combine.hip", "rows.h", "common.h"],
-             "k_dispatch_bf16": ["dispatch.hip", "rows.h", "common.h"],
-             "k_dispatch_mxfp4": ["dispatch.hip", "rows.h", "common.h"]}.get(kernel, [])
+    files = (["combine.hip", "rows.h", "common.h"] if kernel.startswith("k_combine") else
+             ["dispatch.hip", "rows.h", "common.h"] if kernel.startswith("k_dispatch") else [])
     hsh = hashlib.sha256()
     for f in files:
         with open(os.path.join(csrc, f), encoding="utf-8") as fh:
@@ -430,8 +442,8 @@ def main():
     for pname, pl in pipelines.items():
         log(f"{pname} pipeline: {pl['ms']:.3f} ms/pass, {pl['gbps']} GB/s ({pl['frac_of_peak'] * 100:.1f}% of peak)")
 
-    dom = max(KERNEL_OF_STAGE, key=lambda nm: stage_ms[nm])
-    kern = KERNEL_OF_STAGE[dom]
+    dom = max(ROW_STAGES, key=lambda nm: stage_ms[nm])
+    kern = kernel_of_stage(dom, w)
     achieved = bts[dom] / (stage_ms[dom] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": kern, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -40,9 +40,9 @@ namespace {
 constexpr int kDispatchThreads = MOE_DISPATCH_THREADS;
 constexpr int kMxThreads = MOE_MXFP4_THREADS;
 // Store policy of the bf16 kernels, by output size (measured on MI355X).
-// Mid-size outputs, [kPlainMinBytes, kStreamMinBytes), use plain stores,
-// which the 256 MB Infinity Cache absorbs in good part while they drain, and
-// load x only for routed tokens.  Smaller outputs (latency-bound: plain
+// Outputs that fit in the 256 MB Infinity Cache, [kPlainMinBytes,
+// kStreamMinBytes), use plain stores, which it can absorb while they drain,
+// and load x only for routed tokens.  Smaller outputs (latency-bound: plain
 // stores leave dirty L2 lines to write back when the kernel ends) and larger
 // ones (a stream through HBM) use non-temporal stores and load x before the
 // positions arrive.
@@ -50,7 +50,7 @@ constexpr int kMxThreads = MOE_MXFP4_THREADS;
 #define MOE_DISPATCH_PLAIN_MIN_BYTES (int64_t(64) << 20)
 #endif
 #ifndef MOE_DISPATCH_STREAM_MIN_BYTES
-#define MOE_DISPATCH_STREAM_MIN_BYTES (int64_t(1) << 30)
+#define MOE_DISPATCH_STREAM_MIN_BYTES (int64_t(256) << 20)
 #endif
 constexpr int64_t kPlainMinBytes = MOE_DISPATCH_PLAIN_MIN_BYTES;
 constexpr int64_t kStreamMinBytes = MOE_DISPATCH_STREAM_MIN_BYTES;

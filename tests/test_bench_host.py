@@ -63,3 +63,20 @@ def test_source_digest_ignores_comments(tmp_path, monkeypatch):
     assert bench.source_digest("k_combine") == d0
     (csrc / "combine.hip").write_text(text.replace("kBatch = 8", "kBatch = 4"))
     assert bench.source_digest("k_combine") != d0
+
+
+def test_kernel_labels_follow_the_launch_rule():
+    """The roofline label names the kernel the library launches: the
+    loop-free bf16 dispatch for top_k <= 8, the loop-free combine below
+    1 GiB of routed y rows, whole-row combine above."""
+    by = workloads.BY_NAME
+    stress, decode = by["large_prefill_stress"], by["decode"]
+    assert bench.kernel_of_stage("dispatch_bf16", stress) == "k_dispatch_bf16_parts"
+    assert bench.kernel_of_stage("combine", stress) == "k_combine"
+    assert bench.kernel_of_stage("combine", decode) == "k_combine_parts"
+    assert bench.kernel_of_stage("dispatch_mxfp4", decode) == "k_dispatch_mxfp4"
+    wide = workloads.scaled(decode, top_k=9)
+    assert bench.kernel_of_stage("dispatch_bf16", wide) == "k_dispatch_bf16"
+    assert bench.kernel_of_stage("combine", wide) == "k_combine"
+    assert bench.source_digest("k_combine_parts") == bench.source_digest("k_combine")
+    assert bench.source_digest("k_dispatch_bf16_parts") == bench.source_digest("k_dispatch_mxfp4")
