@@ -186,6 +186,39 @@ def test_combine_epilogue(scale, with_residual, k):
     _combine_epi_case(300, k, 16, 7168 // 7, scale, with_residual, 60 + k)
 
 
+def test_combine_epilogue_whole_rows_sampled():
+    """top_k = 8 with over 1 GiB of routed y rows (9400 tokens, H = 7168),
+    which the whole-row combine kernel takes: the epilogue with a residual on
+    64 sampled tokens (real and fully unrouted ones) against the oracle."""
+    n, k, e, h, scale = 9400, 8, 64, 7168, 0.75
+    print(f"[parity] combine epilogue n={n} k={k} h={h}", flush=True)
+    g = np.random.default_rng(777)
+    ids = g.integers(0, e, size=(n, k)).astype(np.int32)
+    ids[g.choice(n, 40, replace=False)] = -1
+    ref = oracle.create_indices(ids, e)
+    v = ref["n_routed"]
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(778)
+    y = torch.randn((v, h), generator=gen, device=DEV).to(torch.bfloat16)
+    res = (torch.randn((n, h), generator=gen, device=DEV) * 3).to(torch.bfloat16)
+    w = g.random((n, k)).astype(np.float32)
+    restore = torch.from_numpy(ref["restore_token_order"].view(np.int32)).to(DEV).view(torch.uint32)
+    out = torch.empty((n, h), dtype=torch.bfloat16, device=DEV)
+    mod.moe_combine_epilogue(y, torch.from_numpy(w).to(DEV), restore, k, out, scale, res)
+    torch.cuda.synchronize()
+    unrouted = np.flatnonzero((ids < 0).all(axis=1))
+    tok = np.unique(np.concatenate([g.choice(n, 56, replace=False), unrouted[:8]]))
+    pos = ref["restore_token_order"].reshape(n, k)[tok]
+    routed = pos != SENT
+    rows = np.unique(pos[routed]).astype(np.int64)
+    ysub = u16(y[torch.from_numpy(rows).to(DEV)])
+    local = np.full(pos.shape, SENT, dtype=np.uint32)
+    local[routed] = np.searchsorted(rows, pos[routed]).astype(np.uint32)
+    want = oracle.combine_epilogue(ysub, w[tok], local.reshape(-1), k, scale,
+                                   u16(res[torch.from_numpy(tok).to(DEV)]))
+    np.testing.assert_array_equal(u16(out[torch.from_numpy(tok).to(DEV)]), want)
+
+
 def test_combine_epilogue_matches_combine_at_identity():
     w = workloads.WORKLOADS[3]
     ids, wts, real = workloads.make_routing(w, 3)
