@@ -499,6 +499,27 @@ def test_dispatch_rows_beyond_one_item_grid():
     np.testing.assert_array_equal(u16(out[:v]), oracle.dispatch(xb, ref["token_expert_order"], k, v))
 
 
+@pytest.mark.parametrize("n, k, h", [(1500, 12, 2048), (400, 9, 2048), (6000, 8, 1024)])
+def test_dispatch_store_regimes(n, k, h):
+    """Outputs on both sides of the store-policy bounds of bf16 dispatch:
+    under 64 MiB (non-temporal stores, eager x loads) and 64-256 MiB (plain
+    stores, x loaded for routed tokens only), through the looping kernel
+    (k > 8) and the loop-free one (k = 8).  Every routed row against the
+    oracle, with a quarter of the rows unrouted."""
+    e = 64
+    print(f"[parity] dispatch regimes n={n} k={k} h={h} out={n * k * h * 2 / 2**20:.0f} MiB", flush=True)
+    g = np.random.default_rng(n + k)
+    ids = g.integers(0, e, size=(n, k)).astype(np.int32)
+    ids[g.random(n) < 0.25] = -1
+    ref = oracle.create_indices(ids, e)
+    v = ref["n_routed"]
+    xb = oracle.f32_to_bf16_rne(g.standard_normal((n, h)).astype(np.float32))
+    restore = torch.from_numpy(ref["restore_token_order"].view(np.int32)).to(DEV).view(torch.uint32)
+    out = torch.zeros((n * k, h), dtype=torch.bfloat16, device=DEV)
+    mod.moe_dispatch(bf16_from_bits(xb, DEV), k, restore, out)
+    np.testing.assert_array_equal(u16(out[:v]), oracle.dispatch(xb, ref["token_expert_order"], k, v))
+
+
 def test_workspace_reuse_across_shapes():
     """One zero-filled workspace serves calls of different sizes, expert
     counts and id widths in any order: nothing an earlier call left in it is
