@@ -221,7 +221,8 @@ def time_extensions(torch, moe, w, x, y, d_ids, d_w, idx, n_routed, reps):
 
 def time_pipelines(torch, calls, bts, n_routed, steps, warmup, scrub=None, fused_front=None):
     """Each single-format pipeline (mask -> indices -> one dispatch -> combine)
-    run as its own loop of `steps` passes, events around every stage.  A
+    run as its own loop of `steps` passes, events around each pass (and
+    around every stage in a second loop, for the stage times).  A
     stage's writes can still be draining from the memory-side cache when the
     next kernel starts, so only a pipeline's own loop charges it what it
     leaves behind.  With fused_front (the one-call mask + indices), the two
@@ -242,19 +243,30 @@ def time_pipelines(torch, calls, bts, n_routed, steps, warmup, scrub=None, fused
             for f in fns:
                 f()
         torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+        # totals with events at the ends of each pass only; stage times from a second loop
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
         for i in range(steps):
             if scrub is not None:
                 scrub()
-            for j, f in enumerate(fns):
-                ev[i][j].record()
+            ev[i][0].record()
+            for f in fns:
                 f()
-            ev[i][len(fns)].record()
+            ev[i][1].record()
         torch.cuda.synchronize()
-        per = [ev[i][0].elapsed_time(ev[i][len(fns)]) for i in range(steps)]
-        ms = float(np.mean(per)) if scrub is not None else ev[0][0].elapsed_time(ev[-1][len(fns)]) / steps
+        per = [ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]
+        ms = float(np.mean(per)) if scrub is not None else ev[0][0].elapsed_time(ev[-1][1]) / steps
+        n_stage = min(steps, 50)
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(n_stage)]
+        for i in range(n_stage):
+            if scrub is not None:
+                scrub()
+            for j, f in enumerate(fns):
+                sev[i][j].record()
+                f()
+            sev[i][len(fns)].record()
+        torch.cuda.synchronize()
         b = sum(bts[nm] for nm in names)
-        st = {nm: round(float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)])), 4)
+        st = {nm: round(float(np.mean([sev[i][j].elapsed_time(sev[i][j + 1]) for i in range(n_stage)])), 4)
               for j, nm in enumerate(names)}
         res[pname] = {"ms": round(ms, 4), "ms_median": round(float(np.median(per)), 4),
                       "ms_min": round(float(np.min(per)), 4), "slots_per_s": n_routed / (ms * 1e-3), "bytes": b,
@@ -372,11 +384,8 @@ def main():
         if int(idx["expert_usage_stats"][1].item()) > 0 else 0
     log(f"warmup done, routed slots V={n_routed}")
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(args.steps)]
     graph = None
     if args.graph:
-        # stage boundaries are event nodes inside the captured graph
-        graph_ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -392,38 +401,40 @@ def main():
         torch.cuda.synchronize()
         log("captured the step as one graph")
     torch.cuda.synchronize()
+    # the timed steps carry events at their two ends only: an event recorded
+    # between two kernels costs a few microseconds of queue processing, which
+    # latency-bound steps would otherwise be charged
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         if scrub is not None:
             scrub()
+        ev[i][0].record()
         if graph is not None:
-            ev[i][0].record()
             graph.replay()
-            for j in range(1, len(STAGES) + 1):
-                ev[i][j].record()
-            continue
-        for j, c in enumerate(calls):
-            ev[i][j].record()
-            c()
-        ev[i][len(STAGES)].record()
+        else:
+            for c in calls:
+                c()
+        ev[i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    stage_ms = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
-                for j, name in enumerate(STAGES)}
-    if graph is not None:  # a replay is one unit: per-stage times come from an eager pass of the same step
+    per_step = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
+    step_ms = float(np.mean(per_step))
+    span_ms = ev[0][0].elapsed_time(ev[-1][1]) / args.steps
+    log(f"timed {args.steps} steps: {step_ms:.3f} ms/step (events), span {span_ms:.3f}, wall {wall / args.steps * 1e3:.3f}")
+    # per-stage times from a separate eager loop with an event before every stage
+    n_stage = min(args.steps, 50)
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(n_stage)]
+    for i in range(n_stage):
         if scrub is not None:
             scrub()
-        eager = [torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
         for j, c in enumerate(calls):
-            eager[j].record()
+            sev[i][j].record()
             c()
-        eager[len(STAGES)].record()
-        torch.cuda.synchronize()
-        stage_ms = {name: eager[j].elapsed_time(eager[j + 1]) for j, name in enumerate(STAGES)}
-    per_step = [ev[i][0].elapsed_time(ev[i][len(STAGES)]) for i in range(args.steps)]
-    step_ms = float(np.mean(per_step))
-    span_ms = ev[0][0].elapsed_time(ev[-1][len(STAGES)]) / args.steps
-    log(f"timed {args.steps} steps: {step_ms:.3f} ms/step (events), span {span_ms:.3f}, wall {wall / args.steps * 1e3:.3f}")
+        sev[i][len(STAGES)].record()
+    torch.cuda.synchronize()
+    stage_ms = {name: float(np.mean([sev[i][j].elapsed_time(sev[i][j + 1]) for i in range(n_stage)]))
+                for j, name in enumerate(STAGES)}
 
     bts = stage_bytes(w, n_routed)
     step_bytes = sum(bts.values())
