@@ -3,8 +3,9 @@
 //
 // The pages' kernel is one CTA.  Here the slots are cut into chunks (of
 // kIdxChunk slots, or half that for inputs up to kIdxSmallMaxSlots so that
-// more workgroups share them); for S <= kIdxChunk one workgroup still does
-// all three steps in one launch, otherwise:
+// more workgroups share them); for S <= kIdxChunk one workgroup of the
+// fewest whole waves that hold the slots does all three steps in one launch
+// (k_index_one), otherwise:
 //   k_index_hist     per chunk (taken by ticket): LDS histogram, then a
 //                    decoupled lookback over earlier chunks gives, per
 //                    bucket, the number of slots in all earlier chunks; the
@@ -18,8 +19,8 @@
 // later call of any shape finds no published word it did not write.
 // Bucket b < E is expert b; bucket E collects the unrouted slots, which land
 // after every routed slot and fill token_expert_order[V, S) with sentinels.
-// For the one-call mask + index entry point, k_index_hist (or the single
-// workgroup) also counts the slots of padding rows as unrouted and writes -1
+// For the one-call mask + index entry point, k_index_hist (or k_index_one)
+// also counts the slots of padding rows as unrouted and writes -1
 // into them, so k_index_scatter reads the masked map.
 #include "common.h"
 #include "internal.h"
@@ -75,7 +76,7 @@ __device__ __forceinline__ uint32_t slot_key(const IdT* ids, IdT* wmap, int64_t 
 
 // Count the chunk's slots per bucket into hist[0..E] (LDS, zeroed by caller).
 // Only totals are needed here, so plain LDS atomics do.
-template <int R, typename IdT>
+template <int R, int T, typename IdT>
 __device__ void chunk_histogram(const IdT* ids, IdT* wmap, int64_t n_slots, int64_t begin,
                                 uint32_t n_experts, uint32_t* hist, int64_t pad_from) {
   const int tid = threadIdx.x;
@@ -83,7 +84,7 @@ __device__ void chunk_histogram(const IdT* ids, IdT* wmap, int64_t n_slots, int6
   bool valid[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int64_t i = begin + int64_t(r) * kIdxThreads + tid;
+    const int64_t i = begin + int64_t(r) * T + tid;
     valid[r] = i < n_slots;
     key[r] = valid[r] ? slot_key(ids, wmap, i, pad_from, n_experts) : 0u;
   }
@@ -133,17 +134,18 @@ __device__ void wave_counts(const IdT* ids, IdT* wmap, int64_t n_slots, int64_t 
 // past its last one.  Turns whist into per-wave running starts (exclusive
 // prefix over waves seeded with the chunk's start), then each slot's position
 // is its wave's running start plus its rank among lower peer lanes.
-template <bool kFromEnd, int R>
+template <bool kFromEnd, int R, int T>
 __device__ void wave_scatter(const WaveTile<R>& tile, uint32_t n_experts, const uint32_t* off,
                              uint32_t* whist, uint32_t* __restrict__ teo,
                              uint32_t* __restrict__ restore, int64_t n_slots) {
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
   const int nb = int(n_experts) + 1;
-  for (int b = tid; b < nb; b += kIdxThreads) {
+  constexpr int kWaves = T / kWave;
+  for (int b = tid; b < nb; b += T) {
     uint32_t run = off[b];
     if (kFromEnd)
-      for (int w = 0; w < kIdxWaves; ++w) run -= whist[w * nb + b];
-    for (int w = 0; w < kIdxWaves; ++w) {
+      for (int w = 0; w < kWaves; ++w) run -= whist[w * nb + b];
+    for (int w = 0; w < kWaves; ++w) {
       const uint32_t c = whist[w * nb + b];
       whist[w * nb + b] = run;
       run += c;
@@ -172,14 +174,16 @@ __device__ void wave_scatter(const WaveTile<R>& tile, uint32_t n_experts, const 
 // base[0..E] (exclusive scan, base[E] = V) and the compacted CSR outputs;
 // with soff given, also the aligned offsets (exclusive scan over active
 // experts of their counts rounded up to `align`).
+template <int T>
 __device__ void finalize_counts(const uint32_t* tot, uint32_t n_experts, uint32_t* base,
                                 uint32_t* __restrict__ esi, int32_t* __restrict__ expert_ids,
                                 uint32_t* __restrict__ stats, uint32_t* __restrict__ soff,
                                 uint32_t align) {
-  __shared__ uint32_t part[4 * kIdxWaves];
+  constexpr int kWaves = T / kWave;
+  __shared__ uint32_t part[4 * kWaves];
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
   const int nb = int(n_experts) + 1;
-  const int ipt = (nb + kIdxThreads - 1) / kIdxThreads;
+  const int ipt = (nb + T - 1) / T;
   const int b0 = tid * ipt;
   const bool want_soff = soff != nullptr;
   uint32_t s_tot = 0, s_act = 0, s_max = 0, s_al = 0;
@@ -201,23 +205,23 @@ __device__ void finalize_counts(const uint32_t* tot, uint32_t n_experts, uint32_
   const uint32_t w_max = wave_max(s_max);
   if (lane == kWave - 1) {
     part[wave] = in_tot;
-    part[kIdxWaves + wave] = in_act;
-    part[2 * kIdxWaves + wave] = w_max;
-    part[3 * kIdxWaves + wave] = in_al;
+    part[kWaves + wave] = in_act;
+    part[2 * kWaves + wave] = w_max;
+    part[3 * kWaves + wave] = in_al;
   }
   __syncthreads();
   uint32_t p_tot = in_tot - s_tot, p_act = in_act - s_act, p_al = in_al - s_al;
   uint32_t all_tot = 0, all_act = 0, all_max = 0, all_al = 0;
-  for (int w = 0; w < kIdxWaves; ++w) {
+  for (int w = 0; w < kWaves; ++w) {
     if (w < wave) {
       p_tot += part[w];
-      p_act += part[kIdxWaves + w];
-      p_al += part[3 * kIdxWaves + w];
+      p_act += part[kWaves + w];
+      p_al += part[3 * kWaves + w];
     }
     all_tot += part[w];
-    all_act += part[kIdxWaves + w];
-    all_max = max(all_max, part[2 * kIdxWaves + w]);
-    all_al += part[3 * kIdxWaves + w];
+    all_act += part[kWaves + w];
+    all_max = max(all_max, part[2 * kWaves + w]);
+    all_al += part[3 * kWaves + w];
   }
   for (int q = 0; q < ipt; ++q) {
     const int b = b0 + q;
@@ -237,8 +241,8 @@ __device__ void finalize_counts(const uint32_t* tot, uint32_t n_experts, uint32_
     }
   }
   const uint32_t n_routed = all_tot - tot[n_experts];
-  for (uint32_t j = all_act + tid; j < n_experts; j += kIdxThreads) expert_ids[j] = -1;
-  for (uint32_t j = all_act + tid; j <= n_experts; j += kIdxThreads) {
+  for (uint32_t j = all_act + tid; j < n_experts; j += T) expert_ids[j] = -1;
+  for (uint32_t j = all_act + tid; j <= n_experts; j += T) {
     esi[j] = n_routed;
     if (want_soff) soff[j] = all_al;
   }
@@ -285,41 +289,47 @@ __device__ uint32_t lookback(const uint64_t* flags, int64_t c, int nb, int b, ui
 
 }  // namespace
 
-// Chunks are R rounds of kIdxThreads slots.
-// n_chunks == 1: one workgroup does histogram, scan and scatter.
-// n_chunks > 1: histogram + lookback + (last ticket) CSR outputs; the
-// scatter follows in k_index_scatter.
+// Inputs of up to R * T slots: one workgroup of T lanes counts per wave,
+// totals the counts, scans them and scatters, in one launch.
+template <typename IdT, int R, int T>
+__global__ __launch_bounds__(T) void k_index_one(
+    const IdT* ids, int64_t n_slots, uint32_t n_experts, int nbits, uint32_t* __restrict__ esi,
+    int32_t* __restrict__ expert_ids, uint32_t* __restrict__ stats, uint32_t* __restrict__ soff,
+    uint32_t align, uint32_t* __restrict__ teo, uint32_t* __restrict__ restore, PadMask pad,
+    IdT* wmap) {
+  extern __shared__ uint32_t lds[];
+  constexpr int kWaves = T / kWave;
+  const int nb = int(n_experts) + 1;
+  uint32_t* hist = lds;
+  uint32_t* base = lds + nb;
+  uint32_t* whist = lds + 2 * nb;
+  WaveTile<R> tile;
+  wave_counts(ids, wmap, n_slots, 0, n_experts, nbits, whist, tile, pad_begin(pad, n_slots));
+  __syncthreads();
+  for (int b = threadIdx.x; b < nb; b += T) {
+    uint32_t t = 0;
+    for (int w = 0; w < kWaves; ++w) t += whist[w * nb + b];
+    hist[b] = t;
+  }
+  __syncthreads();
+  finalize_counts<T>(hist, n_experts, base, esi, expert_ids, stats, soff, align);
+  __syncthreads();
+  wave_scatter<false, R, T>(tile, n_experts, base, whist, teo, restore, n_slots);
+}
+
+// Chunks of R rounds of kIdxThreads slots: histogram + lookback + (last
+// ticket) CSR outputs; the scatter follows in k_index_scatter.
 template <typename IdT, int R>
 __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
     const IdT* ids, int64_t n_slots, uint32_t n_experts, int nbits,
     int64_t n_chunks, IndexWorkspace ws, uint32_t* __restrict__ esi,
     int32_t* __restrict__ expert_ids, uint32_t* __restrict__ stats, uint32_t* __restrict__ soff,
-    uint32_t align, uint32_t* __restrict__ teo, uint32_t* __restrict__ restore, PadMask pad,
-    IdT* wmap) {
+    uint32_t align, PadMask pad, IdT* wmap) {
   extern __shared__ uint32_t lds[];
   __shared__ int64_t s_chunk;
   const int nb = int(n_experts) + 1;
   const int tid = threadIdx.x;
   uint32_t* hist = lds;
-
-  if (n_chunks == 1) {
-    // one workgroup: count per wave, total the counts, scan, scatter
-    uint32_t* base = lds + nb;
-    uint32_t* whist = lds + 2 * nb;
-    WaveTile<R> tile;
-    wave_counts(ids, wmap, n_slots, 0, n_experts, nbits, whist, tile, pad_begin(pad, n_slots));
-    __syncthreads();
-    for (int b = tid; b < nb; b += kIdxThreads) {
-      uint32_t t = 0;
-      for (int w = 0; w < kIdxWaves; ++w) t += whist[w * nb + b];
-      hist[b] = t;
-    }
-    __syncthreads();
-    finalize_counts(hist, n_experts, base, esi, expert_ids, stats, soff, align);
-    __syncthreads();
-    wave_scatter<false>(tile, n_experts, base, whist, teo, restore, n_slots);
-    return;
-  }
 
   if (tid == 0) {
     s_chunk = int64_t(__hip_atomic_fetch_add(ws.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
@@ -331,7 +341,7 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
     if (tid == 0) atomicOr(ws.err, 2u);
     return;
   }
-  chunk_histogram<R>(ids, wmap, n_slots, c * (int64_t(R) * kIdxThreads), n_experts, hist,
+  chunk_histogram<R, kIdxThreads>(ids, wmap, n_slots, c * (int64_t(R) * kIdxThreads), n_experts, hist,
                      pad_begin(pad, n_slots));
   __syncthreads();
 
@@ -351,7 +361,7 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
   __syncthreads();
 
   if (c == n_chunks - 1) {
-    finalize_counts(hist, n_experts, ws.base, esi, expert_ids, stats, soff, align);
+    finalize_counts<kIdxThreads>(hist, n_experts, ws.base, esi, expert_ids, stats, soff, align);
     if (tid == 0)  // every ticket of this call is taken: reset for the next call
       __hip_atomic_store(ws.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -392,7 +402,7 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scatter(
     if (b < nb) off[b] = offv[q];
   }
   __syncthreads();
-  wave_scatter<true>(tile, n_experts, off, lds + nb, teo, restore, n_slots);
+  wave_scatter<true, R, kIdxThreads>(tile, n_experts, off, lds + nb, teo, restore, n_slots);
 }
 
 // Rounds per chunk: up to kIdxChunk slots one workgroup takes them all; up to
@@ -446,12 +456,24 @@ hipError_t launch_chunks(const IdT* ids, int64_t n_slots, int n_experts, int nbi
   const int nb = n_experts + 1;
   hipLaunchKernelGGL((k_index_hist<IdT, R>), dim3(uint32_t(chunks)), dim3(kIdxThreads),
                      size_t(nb) * sizeof(uint32_t), s, ids, n_slots, uint32_t(n_experts), nbits,
-                     chunks, ws, esi, expert_ids, stats, soff, align, teo, restore, pad, wmap);
+                     chunks, ws, esi, expert_ids, stats, soff, align, pad, wmap);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_index_scatter<IdT, R>), dim3(uint32_t(chunks)), dim3(kIdxThreads),
                      size_t(1 + kIdxWaves) * nb * sizeof(uint32_t), s, ids, n_slots,
                      uint32_t(n_experts), nbits, ws, teo, restore);
+  return hipGetLastError();
+}
+
+// The one-workgroup pass with T lanes.
+template <typename IdT, int T>
+hipError_t launch_one(const IdT* ids, int64_t n_slots, int n_experts, int nbits, uint32_t* esi,
+                      int32_t* expert_ids, uint32_t* stats, uint32_t* soff, uint32_t align,
+                      uint32_t* teo, uint32_t* restore, PadMask pad, IdT* wmap, hipStream_t s) {
+  const size_t lds = size_t(2 + T / kWave) * size_t(n_experts + 1) * sizeof(uint32_t);
+  hipLaunchKernelGGL((k_index_one<IdT, kIdxRounds, T>), dim3(1), dim3(T), lds, s, ids, n_slots,
+                     uint32_t(n_experts), nbits, esi, expert_ids, stats, soff, align, teo, restore,
+                     pad, wmap);
   return hipGetLastError();
 }
 
@@ -461,17 +483,22 @@ hipError_t launch_create_indices(const IdT* ids, int64_t n_slots, int n_experts,
                                  uint32_t* stats, uint32_t* soff, uint32_t align, void* wsp,
                                  PadMask pad, hipStream_t s) {
   const int64_t chunks = index_chunks(n_slots);
-  const int nb = n_experts + 1;
   const int nbits = 32 - __builtin_clz(uint32_t(n_experts));
   const IndexWorkspace ws = index_workspace_carve(wsp, n_slots, n_experts);
   // when masking, the map was handed in writable (the fused mask + index call)
   IdT* wmap = pad.count != nullptr ? const_cast<IdT*>(ids) : nullptr;
   if (chunks == 1) {
-    const size_t lds = size_t(2 + kIdxWaves) * nb * sizeof(uint32_t);
-    hipLaunchKernelGGL((k_index_hist<IdT, kIdxRounds>), dim3(1), dim3(kIdxThreads), lds, s, ids,
-                       n_slots, uint32_t(n_experts), nbits, chunks, ws, esi, expert_ids, stats, soff,
-                       align, teo, restore, pad, wmap);
-    return hipGetLastError();
+    // the fewest whole waves of kIdxRounds rounds that hold the slots
+    const int64_t lanes = (n_slots + kIdxRounds - 1) / kIdxRounds;
+#define MOE_INDEX_ONE(TT) \
+  launch_one<IdT, TT>(ids, n_slots, n_experts, nbits, esi, expert_ids, stats, soff, align, teo, \
+                      restore, pad, wmap, s)
+    if (lanes <= 64) return MOE_INDEX_ONE(64);
+    if (lanes <= 128) return MOE_INDEX_ONE(128);
+    if (lanes <= 256) return MOE_INDEX_ONE(256);
+    if (lanes <= 512) return MOE_INDEX_ONE(512);
+    return MOE_INDEX_ONE(kIdxThreads);
+#undef MOE_INDEX_ONE
   }
   if (index_rounds(n_slots) == kIdxSmallRounds)
     return launch_chunks<IdT, kIdxSmallRounds>(ids, n_slots, n_experts, nbits, chunks, ws, esi,

@@ -12,15 +12,15 @@ namespace moe {
 // One workgroup of kIdxThreads threads owns a chunk of kIdxChunk consecutive
 // slots; each of its waves owns kIdxRounds*64 consecutive slots of the chunk.
 #ifndef MOE_IDX_THREADS
-#define MOE_IDX_THREADS 512
+#define MOE_IDX_THREADS 1024
 #endif
 #ifndef MOE_IDX_ROUNDS
-#define MOE_IDX_ROUNDS 4
+#define MOE_IDX_ROUNDS 2
 #endif
 // Inputs of (kIdxChunk, kIdxSmallMaxSlots] slots use chunks of
 // kIdxSmallRounds rounds instead, so that more workgroups share them.
 #ifndef MOE_IDX_SMALL_ROUNDS
-#define MOE_IDX_SMALL_ROUNDS 2
+#define MOE_IDX_SMALL_ROUNDS 1
 #endif
 #ifndef MOE_IDX_SMALL_MAX_SLOTS
 #define MOE_IDX_SMALL_MAX_SLOTS 65536

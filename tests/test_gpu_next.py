@@ -288,6 +288,27 @@ def test_fused_mask_indices_edges(n, k, e, real, tp_rank):
     _check_fused(ids, real, tp_rank, e)
 
 
+# The one-workgroup index pass launches the fewest whole waves that hold the
+# slots (2 per lane): each side of every wave-count step, up to the largest
+# one-workgroup input (2048 slots) and the first two-chunk input.
+@pytest.mark.parametrize("s", [1, 128, 129, 256, 257, 512, 513, 1024, 1025, 2047, 2048, 2049])
+@pytest.mark.parametrize("e", [8, 1024])
+def test_indices_one_workgroup_sizes(s, e):
+    g = np.random.default_rng(s * 7 + e)
+    ids = g.integers(-1, e + 1, size=(s, 1)).astype(np.int32)
+    print(f"[parity] one-workgroup indices: S={s} E={e}", flush=True)
+    d = torch.from_numpy(ids.reshape(-1)).to(DEV)
+    idx = mod.alloc_indices(s, e, DEV, scales_offset=True)
+    mod.moe_create_indices(d, e, idx["token_expert_order"], idx["expert_start_indices"], idx["restore_token_order"],
+                           idx["expert_ids"], idx["expert_usage_stats"], idx["workspace"], idx["scales_offset"], 16)
+    torch.cuda.synchronize()
+    ref = oracle.create_indices(ids, e, scales_align=16)
+    check_indices(idx, ref)
+    np.testing.assert_array_equal(u32(idx["scales_offset"]), ref["scales_offset"])
+    # the one-call mask + indices on the same slots as rows of 1, masking the last third
+    _check_fused(ids, s - s // 3, 0, e, 16)
+
+
 @pytest.mark.parametrize("align", [1, 128])
 def test_fused_mask_indices_int64_and_offsets(align):
     n, k, e, real = 5000, 8, 256, 4321
