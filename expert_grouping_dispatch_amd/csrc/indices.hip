@@ -5,23 +5,34 @@
 // kIdxChunk slots, or half that for inputs up to kIdxSmallMaxSlots so that
 // more workgroups share them); for S <= kIdxChunk one workgroup of the
 // fewest whole waves that hold the slots does all three steps in one launch
-// (k_index_one), otherwise:
-//   k_index_hist     per chunk (taken by ticket): LDS histogram, then a
-//                    decoupled lookback over earlier chunks gives, per
-//                    bucket, the number of slots in all earlier chunks; the
-//                    chunk holding the last ticket also has the totals and
-//                    writes the CSR / active-expert / stats outputs;
-//   k_index_scatter  per chunk: stable ranks (wave ballots + per-wave LDS
-//                    counters) -> token_expert_order and restore_token_order.
-// The workspace layout does not depend on the call's shape (header, bucket
-// starts, then the lookback words), and k_index_scatter zeroes every lookback
-// word it has read, so between calls the word region holds zeros only and a
-// later call of any shape finds no published word it did not write.
+// (k_index_one).  More chunks take two launches, one workgroup per chunk:
+//   up to kIdxSumMaxChunks chunks with a count table of at most
+//   kIdxSumMaxEntries entries (every workload here), without waits:
+//     k_index_count        LDS histogram -> one row of 16-bit counts;
+//     k_index_scatter_sum  sums the whole table (totals -> bucket starts;
+//                          rows before its chunk -> its offsets), chunk 0
+//                          writes the CSR / active-expert / stats outputs,
+//                          then the stable scatter;
+//   larger inputs, where that table would be read too many times:
+//     k_index_hist     per chunk (taken by ticket): LDS histogram, then a
+//                      decoupled lookback over earlier chunks gives, per
+//                      bucket, the number of slots in all earlier chunks; the
+//                      chunk holding the last ticket also has the totals and
+//                      writes the CSR / active-expert / stats outputs;
+//     k_index_scatter  per chunk: stable ranks -> token_expert_order and
+//                      restore_token_order.
+// Stable ranks come from wave ballots and per-wave LDS counters.  The
+// workspace layout does not depend on the call's shape (header, bucket
+// starts, the count table at its largest, then the lookback words), and
+// k_index_scatter zeroes every lookback word it has read, so between calls
+// the word region holds zeros only and a later call of any shape finds no
+// published word it did not write.  The count table is rewritten by every
+// call that reads it.
 // Bucket b < E is expert b; bucket E collects the unrouted slots, which land
 // after every routed slot and fill token_expert_order[V, S) with sentinels.
-// For the one-call mask + index entry point, k_index_hist (or k_index_one)
-// also counts the slots of padding rows as unrouted and writes -1
-// into them, so k_index_scatter reads the masked map.
+// For the one-call mask + index entry point, the first kernel also counts the
+// slots of padding rows as unrouted and writes -1 into them, so the scatter
+// reads the masked map.
 #include "common.h"
 #include "internal.h"
 
@@ -62,14 +73,34 @@ __device__ __forceinline__ int64_t pad_begin(const PadMask& pad, int64_t n_slots
   return first * pad.top_k;
 }
 
-// Bucket of slot i; slots at or past pad_from are padding: unrouted, and
-// set to -1 through wmap (the same map, writable) when masking.  Each slot
-// is read and written by the same thread, and no other workgroup of the
-// kernel reads it.
+// The ids of R slots, loaded before any is used so that the loads of all
+// rounds are in flight together.  A lane past the last slot loads the last
+// slot again (in bounds) and its value is never used.  Only the
+// one-workgroup pass can have no slots (kMayBeEmpty): then nothing is loaded.
+// Elsewhere the loads take no branch, which would make each one wait.
+template <bool kMayBeEmpty, int R, typename IdT>
+__device__ __forceinline__ void load_ids(const IdT* ids, int64_t n_slots, int64_t first,
+                                         int64_t stride, IdT (&id)[R]) {
+  if (kMayBeEmpty && n_slots == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) id[r] = IdT(0);
+    return;
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t i = first + r * stride;
+    id[r] = ids[i < n_slots ? i : n_slots - 1];
+  }
+}
+
+// Bucket of slot i with id `id`; slots at or past pad_from are padding:
+// unrouted, and set to -1 through wmap (the same map, writable) when masking.
+// Each slot is read and written by the same thread, and no other workgroup of
+// the kernel reads it.
 template <typename IdT>
-__device__ __forceinline__ uint32_t slot_key(const IdT* ids, IdT* wmap, int64_t i, int64_t pad_from,
+__device__ __forceinline__ uint32_t slot_key(IdT id, IdT* wmap, int64_t i, int64_t pad_from,
                                              uint32_t n_experts) {
-  if (i < pad_from) return bucket_of(ids[i], n_experts);
+  if (i < pad_from) return bucket_of(id, n_experts);
   if (wmap != nullptr) wmap[i] = IdT(-1);
   return n_experts;
 }
@@ -80,13 +111,15 @@ template <int R, int T, typename IdT>
 __device__ void chunk_histogram(const IdT* ids, IdT* wmap, int64_t n_slots, int64_t begin,
                                 uint32_t n_experts, uint32_t* hist, int64_t pad_from) {
   const int tid = threadIdx.x;
+  IdT id[R];
+  load_ids<false, R>(ids, n_slots, begin + tid, T, id);
   uint32_t key[R];
   bool valid[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t i = begin + int64_t(r) * T + tid;
     valid[r] = i < n_slots;
-    key[r] = valid[r] ? slot_key(ids, wmap, i, pad_from, n_experts) : 0u;
+    key[r] = valid[r] ? slot_key(id[r], wmap, i, pad_from, n_experts) : 0u;
   }
 #pragma unroll
   for (int r = 0; r < R; ++r)
@@ -105,28 +138,54 @@ struct WaveTile {
   int64_t wbegin;
 };
 
-// Load the wave's keys and count them per bucket into its own LDS row
-// whist[wave][0..E] (only this wave touches the row; no atomics).
+// The ids of the wave's slots of a chunk starting at `begin`.
+template <bool kMayBeEmpty, int R, typename IdT>
+__device__ __forceinline__ void wave_load_ids(const IdT* ids, int64_t n_slots, int64_t begin,
+                                              IdT (&id)[R]) {
+  const int wave = threadIdx.x / kWave;
+  load_ids<kMayBeEmpty, R>(ids, n_slots, begin + int64_t(wave) * R * kWave + __lane_id(), kWave, id);
+}
+
+// The tile's keys from the ids wave_load_ids loaded (the keys of padding
+// slots are the unrouted bucket; with wmap given, those slots are set to -1).
 template <int R, typename IdT>
-__device__ void wave_counts(const IdT* ids, IdT* wmap, int64_t n_slots, int64_t begin,
-                            uint32_t n_experts, int nbits, uint32_t* whist, WaveTile<R>& tile,
-                            int64_t pad_from) {
+__device__ __forceinline__ void wave_keys(const IdT (&id)[R], IdT* wmap, int64_t n_slots,
+                                          int64_t begin, uint32_t n_experts, WaveTile<R>& tile,
+                                          int64_t pad_from) {
   const int lane = __lane_id(), wave = threadIdx.x / kWave;
-  const int nb = int(n_experts) + 1;
-  uint32_t* my = whist + wave * nb;
   tile.wbegin = begin + int64_t(wave) * R * kWave;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t i = tile.wbegin + r * kWave + lane;
     tile.valid[r] = i < n_slots;
-    tile.key[r] = tile.valid[r] ? slot_key(ids, wmap, i, pad_from, n_experts) : 0u;
+    tile.key[r] = tile.valid[r] ? slot_key(id[r], wmap, i, pad_from, n_experts) : 0u;
   }
+}
+
+// Count the tile's keys per bucket into the wave's own LDS row
+// whist[wave][0..E] (only this wave touches the row; no atomics).
+template <int R>
+__device__ __forceinline__ void wave_count_keys(uint32_t n_experts, int nbits, uint32_t* whist,
+                                                WaveTile<R>& tile) {
+  const int lane = __lane_id(), wave = threadIdx.x / kWave;
+  const int nb = int(n_experts) + 1;
+  uint32_t* my = whist + wave * nb;
   for (int b = lane; b < nb; b += kWave) my[b] = 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     tile.peers[r] = match_peers(tile.key[r], nbits, tile.valid[r]);
     if (tile.valid[r] && is_leader(tile.peers[r])) my[tile.key[r]] += uint32_t(__popcll(tile.peers[r]));
   }
+}
+
+template <bool kMayBeEmpty, int R, typename IdT>
+__device__ void wave_counts(const IdT* ids, IdT* wmap, int64_t n_slots, int64_t begin,
+                            uint32_t n_experts, int nbits, uint32_t* whist, WaveTile<R>& tile,
+                            int64_t pad_from) {
+  IdT id[R];
+  wave_load_ids<kMayBeEmpty>(ids, n_slots, begin, id);
+  wave_keys(id, wmap, n_slots, begin, n_experts, tile, pad_from);
+  wave_count_keys(n_experts, nbits, whist, tile);
 }
 
 // Stable scatter after wave_counts and a barrier.  off[b] (LDS) = position
@@ -171,14 +230,14 @@ __device__ void wave_scatter(const WaveTile<R>& tile, uint32_t n_experts, const 
 }
 
 // Block-wide: from per-bucket totals tot[0..E] (LDS) write the bucket starts
-// base[0..E] (exclusive scan, base[E] = V) and the compacted CSR outputs;
-// with soff given, also the aligned offsets (exclusive scan over active
-// experts of their counts rounded up to `align`).
+// base[0..E] (exclusive scan, base[E] = V) and, when `outputs` is set, the
+// compacted CSR outputs; with soff given, also the aligned offsets
+// (exclusive scan over active experts of their counts rounded up to `align`).
 template <int T>
 __device__ void finalize_counts(const uint32_t* tot, uint32_t n_experts, uint32_t* base,
                                 uint32_t* __restrict__ esi, int32_t* __restrict__ expert_ids,
                                 uint32_t* __restrict__ stats, uint32_t* __restrict__ soff,
-                                uint32_t align) {
+                                uint32_t align, bool outputs = true) {
   constexpr int kWaves = T / kWave;
   __shared__ uint32_t part[4 * kWaves];
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
@@ -228,7 +287,7 @@ __device__ void finalize_counts(const uint32_t* tot, uint32_t n_experts, uint32_
     if (b < nb) {
       const uint32_t v = tot[b];
       base[b] = p_tot;
-      if (b < int(n_experts) && v > 0) {
+      if (outputs && b < int(n_experts) && v > 0) {
         expert_ids[p_act] = b;
         esi[p_act] = p_tot;
         if (want_soff) {
@@ -240,6 +299,7 @@ __device__ void finalize_counts(const uint32_t* tot, uint32_t n_experts, uint32_
       p_tot += v;
     }
   }
+  if (!outputs) return;
   const uint32_t n_routed = all_tot - tot[n_experts];
   for (uint32_t j = all_act + tid; j < n_experts; j += T) expert_ids[j] = -1;
   for (uint32_t j = all_act + tid; j <= n_experts; j += T) {
@@ -304,7 +364,7 @@ __global__ __launch_bounds__(T) void k_index_one(
   uint32_t* base = lds + nb;
   uint32_t* whist = lds + 2 * nb;
   WaveTile<R> tile;
-  wave_counts(ids, wmap, n_slots, 0, n_experts, nbits, whist, tile, pad_begin(pad, n_slots));
+  wave_counts<true>(ids, wmap, n_slots, 0, n_experts, nbits, whist, tile, pad_begin(pad, n_slots));
   __syncthreads();
   for (int b = threadIdx.x; b < nb; b += T) {
     uint32_t t = 0;
@@ -394,7 +454,7 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scatter(
   }
   WaveTile<R> tile;
   // the map was masked by k_index_hist, so it is read as it is now
-  wave_counts(ids, static_cast<IdT*>(nullptr), n_slots, c * (int64_t(R) * kIdxThreads), n_experts,
+  wave_counts<false>(ids, static_cast<IdT*>(nullptr), n_slots, c * (int64_t(R) * kIdxThreads), n_experts,
               nbits, lds + nb, tile, n_slots);
 #pragma unroll
   for (int q = 0; q < kMaxPerThread; ++q) {
@@ -403,6 +463,114 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scatter(
   }
   __syncthreads();
   wave_scatter<true, R, kIdxThreads>(tile, n_experts, off, lds + nb, teo, restore, n_slots);
+}
+
+// Wait-free path for up to kIdxSumMaxChunks chunks.  k_index_count writes
+// each chunk's slot count per bucket as one row of the count table (16-bit
+// counts, rows of E+1 padded to an even length).  Every k_index_scatter_sum
+// workgroup then reads the whole table: the column sums over all rows are the
+// bucket totals (their scan gives the bucket starts), and the sums over the
+// rows before its chunk give the chunk's offset inside each bucket.  No
+// workgroup waits on another.
+template <typename IdT, int R>
+__global__ __launch_bounds__(kIdxThreads) void k_index_count(
+    const IdT* ids, int64_t n_slots, uint32_t n_experts, uint16_t* __restrict__ counts, PadMask pad,
+    IdT* wmap) {
+  extern __shared__ uint32_t lds[];
+  const int nb = int(n_experts) + 1, nbp = (nb + 1) & ~1;
+  const int c = blockIdx.x;
+  for (int b = threadIdx.x; b < nb; b += kIdxThreads) lds[b] = 0;
+  __syncthreads();
+  chunk_histogram<R, kIdxThreads>(ids, wmap, n_slots, int64_t(c) * (R * kIdxThreads), n_experts, lds,
+                                  pad_begin(pad, n_slots));
+  __syncthreads();
+  uint16_t* row = counts + int64_t(c) * nbp;
+  for (int b = threadIdx.x; b < nbp; b += kIdxThreads) row[b] = uint16_t(b < nb ? lds[b] : 0u);
+}
+
+// Column sums of rows r, r + step, ... < n_rows of the count table (pairs of
+// 16-bit counts, `nw` pairs per row) at pair q, B rows at a time: all B loads
+// are issued before the first is used.  `pre` takes the rows before `before`.
+// Returns the first row not summed.
+template <int B>
+__device__ __forceinline__ int sum_rows(const uint32_t* __restrict__ pairs, int r, int step,
+                                        int n_rows, int nw, int q, int before, uint32_t (&tot)[2],
+                                        uint32_t (&pre)[2]) {
+  for (; r + (B - 1) * step < n_rows; r += B * step) {
+    uint32_t v[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) v[u] = pairs[int64_t(r + u * step) * nw + q];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      tot[0] += v[u] & 0xFFFFu;
+      tot[1] += v[u] >> 16;
+      if (r + u * step < before) {
+        pre[0] += v[u] & 0xFFFFu;
+        pre[1] += v[u] >> 16;
+      }
+    }
+  }
+  return r;
+}
+
+template <typename IdT, int R>
+__global__ __launch_bounds__(kIdxThreads) void k_index_scatter_sum(
+    const IdT* __restrict__ ids, int64_t n_slots, uint32_t n_experts, int nbits, int n_chunks,
+    const uint32_t* __restrict__ pairs, uint32_t* __restrict__ esi, int32_t* __restrict__ expert_ids,
+    uint32_t* __restrict__ stats, uint32_t* __restrict__ soff, uint32_t align,
+    uint32_t* __restrict__ teo, uint32_t* __restrict__ restore) {
+  extern __shared__ uint32_t lds[];
+  const int nb = int(n_experts) + 1, nbp = (nb + 1) & ~1;
+  const int nw = nbp / 2;                                  // count pairs per row
+  const int nwr = (nw + kWave - 1) / kWave * kWave;
+  const int slices = kIdxThreads / nwr;                    // >= 1: nw <= 513
+  const int c = blockIdx.x;
+  uint32_t* tot = lds;                                     // [nbp] totals
+  uint32_t* off = tot + nbp;                               // [nbp] earlier chunks, then start
+  uint32_t* base = off + nbp;                              // [nb]  bucket starts
+  uint32_t* whist = base + nb;                             // [waves][nb]
+  uint32_t* psum = whist + kIdxWaves * nb;                 // [2][slices][nbp]
+
+  // the ids' loads go out first and land while the table is summed
+  const int64_t begin = int64_t(c) * (R * kIdxThreads);
+  IdT id[R];
+  wave_load_ids<false>(ids, n_slots, begin, id);
+
+  // lane q of slice s sums pair q over rows s, s + slices, ...
+  const int slice = threadIdx.x / nwr, q = threadIdx.x - slice * nwr;
+  if (slice < slices && q < nw) {
+    uint32_t t[2] = {0u, 0u}, e[2] = {0u, 0u};
+    int r = sum_rows<16>(pairs, slice, slices, n_chunks, nw, q, c, t, e);
+    r = sum_rows<4>(pairs, r, slices, n_chunks, nw, q, c, t, e);
+    sum_rows<1>(pairs, r, slices, n_chunks, nw, q, c, t, e);
+    uint32_t* pt = psum + slice * nbp;
+    uint32_t* pp = psum + (slices + slice) * nbp;
+    pt[2 * q] = t[0];
+    pt[2 * q + 1] = t[1];
+    pp[2 * q] = e[0];
+    pp[2 * q + 1] = e[1];
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < nbp; b += kIdxThreads) {
+    uint32_t t = 0, e = 0;
+    for (int sl = 0; sl < slices; ++sl) {
+      t += psum[sl * nbp + b];
+      e += psum[(slices + sl) * nbp + b];
+    }
+    tot[b] = t;
+    off[b] = e;
+  }
+  __syncthreads();
+  // every workgroup scans the totals for the bucket starts; chunk 0 also
+  // writes the CSR outputs
+  finalize_counts<kIdxThreads>(tot, n_experts, base, esi, expert_ids, stats, soff, align, c == 0);
+  WaveTile<R> tile;
+  wave_keys(id, static_cast<IdT*>(nullptr), n_slots, begin, n_experts, tile, n_slots);
+  wave_count_keys(n_experts, nbits, whist, tile);
+  __syncthreads();
+  for (int b = threadIdx.x; b < nb; b += kIdxThreads) off[b] += base[b];
+  __syncthreads();
+  wave_scatter<false, R, kIdxThreads>(tile, n_experts, off, whist, teo, restore, n_slots);
 }
 
 // Rounds per chunk: up to kIdxChunk slots one workgroup takes them all; up to
@@ -417,20 +585,27 @@ int64_t index_chunks(int64_t n_slots) {
   return n_slots <= kIdxChunk ? 1 : (n_slots + chunk - 1) / chunk;
 }
 
+bool index_sum_path(int64_t n_slots, int n_experts) {
+  const int64_t chunks = index_chunks(n_slots);
+  const int64_t row = (int64_t(n_experts) + 2) & ~int64_t(1);  // E+1 rounded up to even
+  return chunks > 1 && chunks <= kIdxSumMaxChunks && chunks * row <= kIdxSumMaxEntries;
+}
+
 // Fixed layout for every shape: header words, bucket starts for the largest
-// expert count, then the lookback words [chunks][E+1] of this call.
+// expert count, the count table of the wait-free path at its largest, then
+// the lookback words [chunks][E+1] of this call.
 constexpr size_t kWsHeader = 256;
 constexpr size_t kWsBase = kWsHeader;
-constexpr size_t kWsFlags = kWsBase + ((size_t(MOE_MAX_BUCKETS) * 4 + 255) & ~size_t(255));
+constexpr size_t kWsCounts = kWsBase + ((size_t(MOE_MAX_BUCKETS) * 4 + 255) & ~size_t(255));
+constexpr size_t kWsFlags = kWsCounts + ((size_t(kIdxSumMaxEntries) * 2 + 255) & ~size_t(255));
 
-// Sized for at least as many chunks as any smaller input uses, so that a
-// workspace sized for some n_slots also fits every smaller one.
+// Only the lookback path needs words past the fixed part.  Every input
+// smaller than one that takes the lookback path takes either that path with
+// fewer chunks or no lookback at all, so a workspace sized for some n_slots
+// also fits every smaller one.
 size_t index_workspace_bytes(int64_t n_slots, int n_experts) {
-  int64_t chunks = index_chunks(n_slots);
-  if (n_slots > kIdxSmallMaxSlots) {
-    const int64_t small_most = kIdxSmallMaxSlots / (int64_t(kIdxThreads) * kIdxSmallRounds);
-    chunks = chunks > small_most ? chunks : small_most;
-  }
+  const int64_t chunks = index_chunks(n_slots);
+  if (chunks == 1 || index_sum_path(n_slots, n_experts)) return kWsFlags;
   const size_t c = size_t(chunks), nb = size_t(n_experts) + 1;
   return kWsFlags + align256(c * nb * 8);
 }
@@ -443,6 +618,7 @@ IndexWorkspace index_workspace_carve(void* ws, int64_t n_slots, int n_experts) {
   w.err = reinterpret_cast<uint32_t*>(p);
   w.ticket = reinterpret_cast<uint32_t*>(p + 4);
   w.base = reinterpret_cast<uint32_t*>(p + kWsBase);
+  w.counts = reinterpret_cast<uint16_t*>(p + kWsCounts);
   w.flags = reinterpret_cast<uint64_t*>(p + kWsFlags);
   return w;
 }
@@ -462,6 +638,28 @@ hipError_t launch_chunks(const IdT* ids, int64_t n_slots, int n_experts, int nbi
   hipLaunchKernelGGL((k_index_scatter<IdT, R>), dim3(uint32_t(chunks)), dim3(kIdxThreads),
                      size_t(1 + kIdxWaves) * nb * sizeof(uint32_t), s, ids, n_slots,
                      uint32_t(n_experts), nbits, ws, teo, restore);
+  return hipGetLastError();
+}
+
+// The two launches of the wait-free path, chunks of R rounds.
+template <typename IdT, int R>
+hipError_t launch_sums(const IdT* ids, int64_t n_slots, int n_experts, int nbits, int64_t chunks,
+                       IndexWorkspace ws, uint32_t* esi, int32_t* expert_ids, uint32_t* stats,
+                       uint32_t* soff, uint32_t align, uint32_t* teo, uint32_t* restore,
+                       PadMask pad, IdT* wmap, hipStream_t s) {
+  const int nb = n_experts + 1, nbp = (nb + 1) & ~1;
+  const int nwr = (nbp / 2 + kWave - 1) / kWave * kWave;
+  const int slices = kIdxThreads / nwr;
+  hipLaunchKernelGGL((k_index_count<IdT, R>), dim3(uint32_t(chunks)), dim3(kIdxThreads),
+                     size_t(nb) * sizeof(uint32_t), s, ids, n_slots, uint32_t(n_experts), ws.counts,
+                     pad, wmap);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lds = size_t(2 * nbp + nb + kIdxWaves * nb + 2 * slices * nbp) * sizeof(uint32_t);
+  hipLaunchKernelGGL((k_index_scatter_sum<IdT, R>), dim3(uint32_t(chunks)), dim3(kIdxThreads), lds, s,
+                     ids, n_slots, uint32_t(n_experts), nbits, int(chunks),
+                     reinterpret_cast<const uint32_t*>(ws.counts), esi, expert_ids, stats, soff, align,
+                     teo, restore);
   return hipGetLastError();
 }
 
@@ -499,6 +697,14 @@ hipError_t launch_create_indices(const IdT* ids, int64_t n_slots, int n_experts,
     if (lanes <= 512) return MOE_INDEX_ONE(512);
     return MOE_INDEX_ONE(kIdxThreads);
 #undef MOE_INDEX_ONE
+  }
+  if (index_sum_path(n_slots, n_experts)) {
+    if (index_rounds(n_slots) == kIdxSmallRounds)
+      return launch_sums<IdT, kIdxSmallRounds>(ids, n_slots, n_experts, nbits, chunks, ws, esi,
+                                               expert_ids, stats, soff, align, teo, restore, pad,
+                                               wmap, s);
+    return launch_sums<IdT, kIdxRounds>(ids, n_slots, n_experts, nbits, chunks, ws, esi, expert_ids,
+                                        stats, soff, align, teo, restore, pad, wmap, s);
   }
   if (index_rounds(n_slots) == kIdxSmallRounds)
     return launch_chunks<IdT, kIdxSmallRounds>(ids, n_slots, n_experts, nbits, chunks, ws, esi,

@@ -32,6 +32,18 @@ constexpr int kIdxSmallRounds = MOE_IDX_SMALL_ROUNDS;
 constexpr int64_t kIdxSmallMaxSlots = MOE_IDX_SMALL_MAX_SLOTS;
 constexpr int64_t kIdxChunk = int64_t(kIdxThreads) * kIdxRounds;
 #define MOE_MAX_BUCKETS 1025  // experts + the unrouted bucket
+// Inputs of up to kIdxSumMaxChunks chunks whose count table (chunks rows of
+// E+1 16-bit counts, rows padded to an even length) holds at most
+// kIdxSumMaxEntries entries take the wait-free path: every scatter workgroup
+// sums the count table itself.  Larger inputs chain the chunks by lookback.
+#ifndef MOE_IDX_SUM_MAX_CHUNKS
+#define MOE_IDX_SUM_MAX_CHUNKS 512
+#endif
+#ifndef MOE_IDX_SUM_MAX_ENTRIES
+#define MOE_IDX_SUM_MAX_ENTRIES (1 << 17)
+#endif
+constexpr int64_t kIdxSumMaxChunks = MOE_IDX_SUM_MAX_CHUNKS;
+constexpr int64_t kIdxSumMaxEntries = MOE_IDX_SUM_MAX_ENTRIES;
 
 // The caller zero-fills the workspace once.  The kernels keep it ready for
 // the next call of any shape: the last ticket holder resets the ticket, and
@@ -41,11 +53,14 @@ struct IndexWorkspace {
                         //      ticket past the last chunk (workspace not zero-filled)
   uint32_t* ticket;     // [1]  chunk ticket counter
   uint32_t* base;       // [E+1]         first position of bucket b
+  uint16_t* counts;     // [chunks][E+1 rounded up to even] slots per chunk and bucket
+                        //      (wait-free path; rewritten by every call that uses it)
   uint64_t* flags;      // [chunks][E+1] (status << 32 | count) lookback words
 };
 
 int index_rounds(int64_t n_slots);
 int64_t index_chunks(int64_t n_slots);
+bool index_sum_path(int64_t n_slots, int n_experts);
 size_t index_workspace_bytes(int64_t n_slots, int n_experts);
 IndexWorkspace index_workspace_carve(void* ws, int64_t n_slots, int n_experts);
 

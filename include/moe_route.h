@@ -139,9 +139,9 @@ size_t moe_create_indices_workspace_bytes(int64_t n_slots, int32_t n_experts);
  *                         moe_create_indices_workspace_bytes(S, E) bytes,
  *                         256-byte aligned, zero-filled once before its first
  *                         use; every call leaves it ready for the next one
- *                         (its layout does not depend on S and E, and the
- *                         call zeroes again the part it used, so any S and E
- *                         that fit its size may follow).
+ *                         (its layout does not depend on S and E, and a call
+ *                         reads nothing an earlier call left in it, so any S
+ *                         and E that fit its size may follow).
  *                         Calls that share a workspace must not overlap.
  *                         Its first 32-bit word becomes nonzero (and stays
  *                         so) if a cross-workgroup wait ever gave up or the

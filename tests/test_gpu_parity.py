@@ -337,10 +337,46 @@ def test_deterministic_under_skew():
     assert torch.equal(a["q"], b["q"])
 
 
-def test_lookback_error_word_clear():
-    ids, w, real, x, y = _rand_case(40, 30000, 8, 256, 32, "distinct")
-    res = run_path(mod, ids, real, 256, x, y, w, ("bf16",))
+@pytest.mark.parametrize("n, e", [(30000, 256), (40000, 1024)])   # count-table sums / lookback
+def test_index_error_word_clear(n, e):
+    ids, w, real, x, y = _rand_case(40, n, 8, e, 32, "distinct")
+    res = run_path(mod, ids, real, e, x, y, w, ("bf16",))
     assert int(res["workspace"][:4].view(torch.int32).item()) == 0
+
+
+# The multi-chunk index paths: up to 512 chunks whose count table (chunks x
+# (E+1 rounded up to even) 16-bit counts) holds at most 2^17 entries, every
+# workgroup sums the table; larger inputs chain the chunks by lookback.  Both
+# sides of each limit, with unrouted ids and the separate and one-call forms.
+@pytest.mark.parametrize("s, e", [
+    (508 * 2048, 256), (508 * 2048 + 1, 256),       # 508 * 258 entries; 509 rows are too many
+    (512 * 2048, 8), (512 * 2048 + 1, 8),           # 512 chunks; 513 are too many
+    (127 * 2048, 1024), (127 * 2048 + 1, 1024),     # 127 * 1026 entries; 128 rows are too many
+    (65536, 1024), (65537, 1024),                   # the 1024-slot chunks of mid-size inputs, then 2048
+])
+def test_index_paths_around_the_table_limit(s, e):
+    g = np.random.default_rng(s + e)
+    ids = g.integers(-1, e + 1, size=(s, 1)).astype(np.int32)
+    print(f"[parity] multi-chunk indices: S={s} E={e}", flush=True)
+    d = torch.from_numpy(ids.reshape(-1)).to(DEV)
+    idx = mod.alloc_indices(s, e, DEV, scales_offset=True)
+    mod.moe_create_indices(d, e, idx["token_expert_order"], idx["expert_start_indices"], idx["restore_token_order"],
+                           idx["expert_ids"], idx["expert_usage_stats"], idx["workspace"], idx["scales_offset"], 64)
+    torch.cuda.synchronize()
+    ref = oracle.create_indices(ids, e, scales_align=64)
+    check_indices(idx, ref)
+    np.testing.assert_array_equal(u32(idx["scales_offset"]), ref["scales_offset"])
+    assert int(idx["workspace"][:4].view(torch.int32).item()) == 0
+    # the one-call mask + indices, masking the last 1000 rows, in the same workspace
+    real = s - 1000
+    d = torch.from_numpy(ids.reshape(-1)).to(DEV)
+    mod.moe_mask_create_indices(d.view(s, 1), torch.tensor([real], dtype=torch.int32, device=DEV), 0, e,
+                                idx["token_expert_order"], idx["expert_start_indices"], idx["restore_token_order"],
+                                idx["expert_ids"], idx["expert_usage_stats"], idx["workspace"])
+    torch.cuda.synchronize()
+    m = oracle.mask_routing_padding(ids, real, 0)
+    np.testing.assert_array_equal(d.view(s, 1).cpu().numpy(), m)
+    check_indices(idx, oracle.create_indices(m, e))
 
 
 def test_argument_errors_on_device():
@@ -608,7 +644,7 @@ def test_workspace_not_zero_filled_sets_error_word():
     them.  The waits are bounded; the call must finish, keep every write
     inside the buffers (canaries after the outputs and the workspace stay
     intact) and set the sticky error word.  The outputs are unspecified."""
-    n, k, e = 100000, 2, 16                     # 200000 slots: the many-workgroup path
+    n, k, e = 600000, 2, 16                     # 1.2M slots, 586 chunks: the lookback path
     s = n * k
     ids = np.random.default_rng(5).integers(0, e, size=(n, k)).astype(np.int32)
     d_ids = torch.from_numpy(ids).to(DEV)
