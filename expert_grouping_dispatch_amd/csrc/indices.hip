@@ -467,7 +467,8 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scatter(
 
 // Wait-free path for up to kIdxSumMaxChunks chunks.  k_index_count writes
 // each chunk's slot count per bucket as one row of the count table (16-bit
-// counts, rows of E+1 padded to an even length).  Every k_index_scatter_sum
+// counts, rows of E+1 padded to a multiple of 8, so that a row is whole
+// 16-byte vectors).  Every k_index_scatter_sum
 // workgroup then reads the whole table: the column sums over all rows are the
 // bucket totals (their scan gives the bucket starts), and the sums over the
 // rows before its chunk give the chunk's offset inside each bucket.  No
@@ -477,7 +478,7 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_count(
     const IdT* ids, int64_t n_slots, uint32_t n_experts, uint16_t* __restrict__ counts, PadMask pad,
     IdT* wmap) {
   extern __shared__ uint32_t lds[];
-  const int nb = int(n_experts) + 1, nbp = (nb + 1) & ~1;
+  const int nb = int(n_experts) + 1, nbp = (nb + 7) & ~7;
   const int c = blockIdx.x;
   for (int b = threadIdx.x; b < nb; b += kIdxThreads) lds[b] = 0;
   __syncthreads();
@@ -488,25 +489,30 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_count(
   for (int b = threadIdx.x; b < nbp; b += kIdxThreads) row[b] = uint16_t(b < nb ? lds[b] : 0u);
 }
 
-// Column sums of rows r, r + step, ... < n_rows of the count table (pairs of
-// 16-bit counts, `nw` pairs per row) at pair q, B rows at a time: all B loads
-// are issued before the first is used.  `pre` takes the rows before `before`.
-// Returns the first row not summed.
+// Column sums at vector q of rows r, r + step, ... < n_rows of the count
+// table (16-byte vectors of eight 16-bit counts, `nw` vectors per row), B
+// rows at a time: all B loads are issued before the first is used.  `pre`
+// takes the rows before `before`.  Returns the first row not summed.
 template <int B>
-__device__ __forceinline__ int sum_rows(const uint32_t* __restrict__ pairs, int r, int step,
-                                        int n_rows, int nw, int q, int before, uint32_t (&tot)[2],
-                                        uint32_t (&pre)[2]) {
+__device__ __forceinline__ int sum_rows(const u32x4* __restrict__ rows, int r, int step, int n_rows,
+                                        int nw, int q, int before, uint32_t (&tot)[8],
+                                        uint32_t (&pre)[8]) {
   for (; r + (B - 1) * step < n_rows; r += B * step) {
-    uint32_t v[B];
+    u32x4 v[B];
 #pragma unroll
-    for (int u = 0; u < B; ++u) v[u] = pairs[int64_t(r + u * step) * nw + q];
+    for (int u = 0; u < B; ++u) v[u] = rows[int64_t(r + u * step) * nw + q];
 #pragma unroll
     for (int u = 0; u < B; ++u) {
-      tot[0] += v[u] & 0xFFFFu;
-      tot[1] += v[u] >> 16;
-      if (r + u * step < before) {
-        pre[0] += v[u] & 0xFFFFu;
-        pre[1] += v[u] >> 16;
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      const bool earlier = r + u * step < before;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        tot[2 * k] += w[k] & 0xFFFFu;
+        tot[2 * k + 1] += w[k] >> 16;
+        if (earlier) {
+          pre[2 * k] += w[k] & 0xFFFFu;
+          pre[2 * k + 1] += w[k] >> 16;
+        }
       }
     }
   }
@@ -516,49 +522,43 @@ __device__ __forceinline__ int sum_rows(const uint32_t* __restrict__ pairs, int 
 template <typename IdT, int R>
 __global__ __launch_bounds__(kIdxThreads) void k_index_scatter_sum(
     const IdT* __restrict__ ids, int64_t n_slots, uint32_t n_experts, int nbits, int n_chunks,
-    const uint32_t* __restrict__ pairs, uint32_t* __restrict__ esi, int32_t* __restrict__ expert_ids,
+    const u32x4* __restrict__ rows, uint32_t* __restrict__ esi, int32_t* __restrict__ expert_ids,
     uint32_t* __restrict__ stats, uint32_t* __restrict__ soff, uint32_t align,
     uint32_t* __restrict__ teo, uint32_t* __restrict__ restore) {
   extern __shared__ uint32_t lds[];
-  const int nb = int(n_experts) + 1, nbp = (nb + 1) & ~1;
-  const int nw = nbp / 2;                                  // count pairs per row
+  const int nb = int(n_experts) + 1, nbp = (nb + 7) & ~7;
+  const int nw = nbp / 8;                                  // 16-byte vectors per row
   const int nwr = (nw + kWave - 1) / kWave * kWave;
-  const int slices = kIdxThreads / nwr;                    // >= 1: nw <= 513
+  const int slices = kIdxThreads / nwr;                    // >= 1: nw <= 129
   const int c = blockIdx.x;
   uint32_t* tot = lds;                                     // [nbp] totals
   uint32_t* off = tot + nbp;                               // [nbp] earlier chunks, then start
   uint32_t* base = off + nbp;                              // [nb]  bucket starts
   uint32_t* whist = base + nb;                             // [waves][nb]
-  uint32_t* psum = whist + kIdxWaves * nb;                 // [2][slices][nbp]
 
   // the ids' loads go out first and land while the table is summed
   const int64_t begin = int64_t(c) * (R * kIdxThreads);
   IdT id[R];
   wave_load_ids<false>(ids, n_slots, begin, id);
+  for (int b = threadIdx.x; b < 2 * nbp; b += kIdxThreads) tot[b] = 0;  // tot and off
+  __syncthreads();
 
-  // lane q of slice s sums pair q over rows s, s + slices, ...
+  // lane q of slice s sums vector q over rows s, s + slices, ...
   const int slice = threadIdx.x / nwr, q = threadIdx.x - slice * nwr;
   if (slice < slices && q < nw) {
-    uint32_t t[2] = {0u, 0u}, e[2] = {0u, 0u};
-    int r = sum_rows<16>(pairs, slice, slices, n_chunks, nw, q, c, t, e);
-    r = sum_rows<4>(pairs, r, slices, n_chunks, nw, q, c, t, e);
-    sum_rows<1>(pairs, r, slices, n_chunks, nw, q, c, t, e);
-    uint32_t* pt = psum + slice * nbp;
-    uint32_t* pp = psum + (slices + slice) * nbp;
-    pt[2 * q] = t[0];
-    pt[2 * q + 1] = t[1];
-    pp[2 * q] = e[0];
-    pp[2 * q + 1] = e[1];
-  }
-  __syncthreads();
-  for (int b = threadIdx.x; b < nbp; b += kIdxThreads) {
-    uint32_t t = 0, e = 0;
-    for (int sl = 0; sl < slices; ++sl) {
-      t += psum[sl * nbp + b];
-      e += psum[(slices + sl) * nbp + b];
+    uint32_t t[8] = {}, e[8] = {};
+    // batches of 16 rows, then at most one each of 8, 4, 2 and 1
+    int r = sum_rows<16>(rows, slice, slices, n_chunks, nw, q, c, t, e);
+    r = sum_rows<8>(rows, r, slices, n_chunks, nw, q, c, t, e);
+    r = sum_rows<4>(rows, r, slices, n_chunks, nw, q, c, t, e);
+    r = sum_rows<2>(rows, r, slices, n_chunks, nw, q, c, t, e);
+    sum_rows<1>(rows, r, slices, n_chunks, nw, q, c, t, e);
+    // the slices' sums meet in LDS (returnless atomic adds)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      atomicAdd(&tot[8 * q + k], t[k]);
+      atomicAdd(&off[8 * q + k], e[k]);
     }
-    tot[b] = t;
-    off[b] = e;
   }
   __syncthreads();
   // every workgroup scans the totals for the bucket starts; chunk 0 also
@@ -587,7 +587,7 @@ int64_t index_chunks(int64_t n_slots) {
 
 bool index_sum_path(int64_t n_slots, int n_experts) {
   const int64_t chunks = index_chunks(n_slots);
-  const int64_t row = (int64_t(n_experts) + 2) & ~int64_t(1);  // E+1 rounded up to even
+  const int64_t row = (int64_t(n_experts) + 8) & ~int64_t(7);  // E+1 rounded up to a multiple of 8
   return chunks > 1 && chunks <= kIdxSumMaxChunks && chunks * row <= kIdxSumMaxEntries;
 }
 
@@ -647,18 +647,16 @@ hipError_t launch_sums(const IdT* ids, int64_t n_slots, int n_experts, int nbits
                        IndexWorkspace ws, uint32_t* esi, int32_t* expert_ids, uint32_t* stats,
                        uint32_t* soff, uint32_t align, uint32_t* teo, uint32_t* restore,
                        PadMask pad, IdT* wmap, hipStream_t s) {
-  const int nb = n_experts + 1, nbp = (nb + 1) & ~1;
-  const int nwr = (nbp / 2 + kWave - 1) / kWave * kWave;
-  const int slices = kIdxThreads / nwr;
+  const int nb = n_experts + 1, nbp = (nb + 7) & ~7;
   hipLaunchKernelGGL((k_index_count<IdT, R>), dim3(uint32_t(chunks)), dim3(kIdxThreads),
                      size_t(nb) * sizeof(uint32_t), s, ids, n_slots, uint32_t(n_experts), ws.counts,
                      pad, wmap);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = size_t(2 * nbp + nb + kIdxWaves * nb + 2 * slices * nbp) * sizeof(uint32_t);
+  const size_t lds = size_t(2 * nbp + nb + kIdxWaves * nb) * sizeof(uint32_t);
   hipLaunchKernelGGL((k_index_scatter_sum<IdT, R>), dim3(uint32_t(chunks)), dim3(kIdxThreads), lds, s,
                      ids, n_slots, uint32_t(n_experts), nbits, int(chunks),
-                     reinterpret_cast<const uint32_t*>(ws.counts), esi, expert_ids, stats, soff, align,
+                     reinterpret_cast<const u32x4*>(ws.counts), esi, expert_ids, stats, soff, align,
                      teo, restore);
   return hipGetLastError();
 }

@@ -33,7 +33,7 @@ constexpr int64_t kIdxSmallMaxSlots = MOE_IDX_SMALL_MAX_SLOTS;
 constexpr int64_t kIdxChunk = int64_t(kIdxThreads) * kIdxRounds;
 #define MOE_MAX_BUCKETS 1025  // experts + the unrouted bucket
 // Inputs of up to kIdxSumMaxChunks chunks whose count table (chunks rows of
-// E+1 16-bit counts, rows padded to an even length) holds at most
+// E+1 16-bit counts, rows padded to a multiple of 8) holds at most
 // kIdxSumMaxEntries entries take the wait-free path: every scatter workgroup
 // sums the count table itself.  Larger inputs chain the chunks by lookback.
 #ifndef MOE_IDX_SUM_MAX_CHUNKS
@@ -53,7 +53,7 @@ struct IndexWorkspace {
                         //      ticket past the last chunk (workspace not zero-filled)
   uint32_t* ticket;     // [1]  chunk ticket counter
   uint32_t* base;       // [E+1]         first position of bucket b
-  uint16_t* counts;     // [chunks][E+1 rounded up to even] slots per chunk and bucket
+  uint16_t* counts;     // [chunks][E+1 rounded up to a multiple of 8] slots per chunk and bucket
                         //      (wait-free path; rewritten by every call that uses it)
   uint64_t* flags;      // [chunks][E+1] (status << 32 | count) lookback words
 };

@@ -345,13 +345,14 @@ def test_index_error_word_clear(n, e):
 
 
 # The multi-chunk index paths: up to 512 chunks whose count table (chunks x
-# (E+1 rounded up to even) 16-bit counts) holds at most 2^17 entries, every
-# workgroup sums the table; larger inputs chain the chunks by lookback.  Both
-# sides of each limit, with unrouted ids and the separate and one-call forms.
+# (E+1 rounded up to a multiple of 8) 16-bit counts) holds at most 2^17
+# entries, every workgroup sums the table; larger inputs chain the chunks by
+# lookback.  Both sides of each limit, with unrouted ids and the separate and
+# one-call forms.
 @pytest.mark.parametrize("s, e", [
-    (508 * 2048, 256), (508 * 2048 + 1, 256),       # 508 * 258 entries; 509 rows are too many
+    (496 * 2048, 256), (496 * 2048 + 1, 256),       # 496 * 264 entries; 497 rows are too many
     (512 * 2048, 8), (512 * 2048 + 1, 8),           # 512 chunks; 513 are too many
-    (127 * 2048, 1024), (127 * 2048 + 1, 1024),     # 127 * 1026 entries; 128 rows are too many
+    (127 * 2048, 1024), (127 * 2048 + 1, 1024),     # 127 * 1032 entries; 128 rows are too many
     (65536, 1024), (65537, 1024),                   # the 1024-slot chunks of mid-size inputs, then 2048
 ])
 def test_index_paths_around_the_table_limit(s, e):
