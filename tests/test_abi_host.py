@@ -145,6 +145,21 @@ def test_no_device_is_rejected_after_the_argument_checks():
     assert L.moe_combine(fake, 20, fake, fake, 10, 16, 2, fake, None) == 3
 
 
+def test_workspace_size_follows_the_index_paths():
+    """Inputs of up to 512 chunks (2048 slots each, 1024 up to 65536 slots)
+    whose count table of 16-bit counts (rows of E+1 rounded up to a multiple
+    of 8) holds at most 2^17 entries need only the fixed part of the
+    workspace; larger ones add 8 bytes per (chunk, bucket) lookback word."""
+    f = mod.moe_create_indices_workspace_bytes
+    fixed = f(1, 8)
+    assert fixed == f(2048, 1024) == f(65536, 1024)            # one workgroup; 64 chunks of 1024 slots
+    for s, e in [(496 * 2048, 256), (512 * 2048, 8), (127 * 2048, 1024), (24000, 1024)]:
+        assert f(s, e) == fixed, (s, e)
+    for s, e, chunks in [(496 * 2048 + 1, 256, 497), (512 * 2048 + 1, 8, 513), (127 * 2048 + 1, 1024, 128)]:
+        want = fixed + (chunks * (e + 1) * 8 + 255) // 256 * 256
+        assert f(s, e) == want, (s, e)
+
+
 def test_workspace_size_is_monotone_in_slots():
     """A workspace sized for some slot count fits every smaller one (across the
     switch between chunk sizes too)."""
