@@ -468,11 +468,10 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scatter(
 // Wait-free path for up to kIdxSumMaxChunks chunks.  k_index_count writes
 // each chunk's slot count per bucket as one row of the count table (16-bit
 // counts, rows of E+1 padded to a multiple of 8, so that a row is whole
-// 16-byte vectors).  Every k_index_scatter_sum
-// workgroup then reads the whole table: the column sums over all rows are the
-// bucket totals (their scan gives the bucket starts), and the sums over the
-// rows before its chunk give the chunk's offset inside each bucket.  No
-// workgroup waits on another.
+// 16-byte vectors).  Every k_index_scatter_sum workgroup then reads the whole
+// table: the column sums over all rows are the bucket totals (their scan
+// gives the bucket starts), and the sums over the rows before its chunk give
+// the chunk's offset inside each bucket.  No workgroup waits on another.
 template <typename IdT, int R>
 __global__ __launch_bounds__(kIdxThreads) void k_index_count(
     const IdT* ids, int64_t n_slots, uint32_t n_experts, uint16_t* __restrict__ counts, PadMask pad,
