@@ -17,6 +17,10 @@ namespace moe {
 namespace {
 
 constexpr int kBatch = 8;
+// Vectors per lane of the whole-row kernel, and the cache policy of y loads
+// and of out stores (measured on MI355X: one vector per lane, non-temporal
+// loads and stores; plain loads let the next dispatch run faster but cost
+// combine more).
 #ifndef MOE_COMBINE_UNROLL
 #define MOE_COMBINE_UNROLL 1
 #endif
