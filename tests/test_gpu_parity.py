@@ -643,6 +643,25 @@ def _launch_path(ids, w, real, e, x, y, st):
     return dict(ids=d_ids, dispatch=out, q=q, scales=sc, combine=o, **idx)
 
 
+# Count-table rows hold E+1 counts padded to a multiple of 8: each side of
+# the padding steps, with 1024-slot chunks (9000 slots) and 2048-slot chunks
+# (70000 slots), unrouted ids included.
+@pytest.mark.parametrize("e", [1, 6, 7, 8, 15, 16, 17, 255, 1023, 1024])
+@pytest.mark.parametrize("s", [9000, 70000])
+def test_index_count_table_row_padding(e, s):
+    g = np.random.default_rng(e * 7 + s)
+    ids = g.integers(-1, e + 1, size=(s, 1)).astype(np.int32)
+    print(f"[parity] count-table rows: S={s} E={e}", flush=True)
+    d = torch.from_numpy(ids.reshape(-1)).to(DEV)
+    idx = mod.alloc_indices(s, e, DEV, scales_offset=True)
+    mod.moe_create_indices(d, e, idx["token_expert_order"], idx["expert_start_indices"], idx["restore_token_order"],
+                           idx["expert_ids"], idx["expert_usage_stats"], idx["workspace"], idx["scales_offset"], 32)
+    torch.cuda.synchronize()
+    ref = oracle.create_indices(ids, e, scales_align=32)
+    check_indices(idx, ref)
+    np.testing.assert_array_equal(u32(idx["scales_offset"]), ref["scales_offset"])
+
+
 def test_workspace_not_zero_filled_sets_error_word():
     """Misuse, forced from the host: the ticket word of the workspace is not
     zero, so the first chunks are never handed out and later chunks wait for
