@@ -444,6 +444,13 @@ def main():
     gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     stages = {name: {"ms": round(stage_ms[name], 4), "bytes": bts[name],
                      "gbps": round(bts[name] / (stage_ms[name] * 1e-3) / 1e9, 1)} for name in STAGES}
+    # HBM bytes the counters measured per launch (committed profiles taken on
+    # the current sources), next to the algorithmic figures
+    for name in ROW_STAGES:
+        counted = read_traffic(kernel_of_stage(name, w), w.name)
+        if counted is not None:
+            stages[name]["counter_bytes"] = counted
+            stages[name]["counter_gbps"] = round(counted / (stage_ms[name] * 1e-3) / 1e9, 1)
     def fused_front():
         moe.moe_mask_create_indices(d_ids, d_cnt, 0, e, idx["token_expert_order"], idx["expert_start_indices"],
                                     idx["restore_token_order"], idx["expert_ids"], idx["expert_usage_stats"],
@@ -456,10 +463,12 @@ def main():
     dom = max(ROW_STAGES, key=lambda nm: stage_ms[nm])
     kern = kernel_of_stage(dom, w)
     achieved = bts[dom] / (stage_ms[dom] * 1e-3) / 1e9
+    traffic = read_traffic(kern, w.name)
     roofline = {"bound": "hbm", "kernel": kern, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": read_traffic(kern, w.name), "algorithmic_bytes_per_launch": bts[dom],
-                "avg_launch_ms": round(stage_ms[dom], 4)}
+                "traffic": traffic, "algorithmic_bytes_per_launch": bts[dom],
+                "avg_launch_ms": round(stage_ms[dom], 4),
+                "traffic_gbps": None if traffic is None else round(traffic / (stage_ms[dom] * 1e-3) / 1e9, 1)}
 
     extensions = None if args.no_extensions else time_extensions(torch, moe, w, x, y, d_ids, d_w, idx, n_routed,
                                                                  args.steps)

@@ -80,3 +80,17 @@ def test_kernel_labels_follow_the_launch_rule():
     assert bench.kernel_of_stage("combine", wide) == "k_combine"
     assert bench.source_digest("k_combine_parts") == bench.source_digest("k_combine")
     assert bench.source_digest("k_dispatch_bf16_parts") == bench.source_digest("k_dispatch_mxfp4")
+
+
+def test_stress_counter_profiles_are_current():
+    """The committed rocprofv3 counter summaries of the three row kernels on
+    the stress workload were taken on the current kernel sources, so the
+    bench reports their measured HBM bytes (and those stay within 2% of the
+    algorithmic bytes: nothing is re-read)."""
+    w = workloads.BY_NAME["large_prefill_stress"]
+    n_routed = w.real_tokens * w.top_k
+    bts = bench.stage_bytes(w, n_routed)
+    for stage in bench.ROW_STAGES:
+        counted = bench.read_traffic(bench.kernel_of_stage(stage, w), w.name)
+        assert counted is not None, stage
+        assert 1.0 <= counted / bts[stage] < 1.02, (stage, counted / bts[stage])
