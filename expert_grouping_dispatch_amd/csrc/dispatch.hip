@@ -37,6 +37,15 @@ namespace {
 #ifndef MOE_MXFP4_PACKED_NT_STORE
 #define MOE_MXFP4_PACKED_NT_STORE 0
 #endif
+// Outputs (payload and scales) under this size, with top_k <= 8, load each
+// lane's first block of x before the token's positions arrive, so that the
+// two loads are in flight together (rows with nothing routed are then read
+// and dropped).  Larger outputs stream through HBM, where the wasted reads
+// and the registers this takes cost more than the overlap saves (measured on
+// MI355X: 3.7% faster on a 125 MB output, 2.5% slower on a 1.9 GB one).
+#ifndef MOE_MXFP4_EAGER_MAX_BYTES
+#define MOE_MXFP4_EAGER_MAX_BYTES (int64_t(256) << 20)
+#endif
 constexpr int kDispatchThreads = MOE_DISPATCH_THREADS;
 constexpr int kMxThreads = MOE_MXFP4_THREADS;
 // Store policy of the bf16 kernels, by output size (measured on MI355X).
@@ -192,7 +201,7 @@ __global__ __launch_bounds__(kDispatchThreads) void k_dispatch_bf16(
 // one scale byte per routed position.  kPacked: one row of 17*nblk bytes per
 // slot, the 16*nblk payload bytes first and the nblk scale bytes after them
 // (the launcher checks 17*nblk % 16 == 0, i.e. hidden % 512 == 0).
-template <int K, bool kEven, bool kPacked>
+template <int K, bool kEven, bool kPacked, bool kEager>
 __global__ __launch_bounds__(kMxThreads) void k_dispatch_mxfp4(
     const u32x4* __restrict__ x, int64_t n_rows, int h16, int top_k,
     const uint32_t* __restrict__ restore, uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
@@ -206,6 +215,16 @@ __global__ __launch_bounds__(kMxThreads) void k_dispatch_mxfp4(
     const int64_t t = rs.split == 1 ? item : item / rs.split;
     const int lo = int(item - t * rs.split) * rs.len;  // this workgroup's blocks [lo, hi)
     const int hi = min(nblk, lo + rs.len);
+    const u32x4* src = x + t * h16;
+    const int b0 = lo + int(threadIdx.x);
+    static_assert(!kEager || K > 0, "eager loads need the positions in registers");
+    u32x4 first[kEager ? 4 : 1];
+    if constexpr (kEager) {
+      if (b0 < hi) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) first[u] = load_vec<MOE_MXFP4_NT_LOAD>(src + 4 * b0 + u);
+      }
+    }
     uint32_t pos[KR];
     float unused[KR];
     int n;
@@ -217,12 +236,11 @@ __global__ __launch_bounds__(kMxThreads) void k_dispatch_mxfp4(
     } else {
       n = gather_routed(restore, nullptr, t, top_k, limit, s_pos, nullptr, &s_n);
     }
-    const u32x4* src = x + t * h16;
-    for (int b = lo + int(threadIdx.x); n > 0 && b < hi; b += kMxThreads) {
+    for (int b = b0; n > 0 && b < hi; b += kMxThreads) {
       uint32_t w[16];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const u32x4 v = load_vec<MOE_MXFP4_NT_LOAD>(src + 4 * b + u);
+        const u32x4 v = (kEager && b == b0) ? first[u] : load_vec<MOE_MXFP4_NT_LOAD>(src + 4 * b + u);
         w[4 * u + 0] = v.x;
         w[4 * u + 1] = v.y;
         w[4 * u + 2] = v.z;
@@ -316,8 +334,17 @@ struct LaunchMxfp4 {
                        const uint32_t* restore, uint8_t* q, uint8_t* scales, uint32_t limit,
                        hipStream_t s) {
     const RowSplit rs = row_split(n_rows, h16 / 4, kMxThreads / 2);
-    hipLaunchKernelGGL((k_dispatch_mxfp4<K, kEven, kPacked>), dim3(row_grid(n_rows * rs.split)),
-                       dim3(kMxThreads), 0, s, x, n_rows, h16, top_k, restore, q, scales, limit, rs);
+    const double out_bytes = double(n_rows) * top_k * (h16 / 4) * 17.0;
+    const dim3 grid(row_grid(n_rows * rs.split)), block(kMxThreads);
+    if constexpr (K > 0) {
+      if (out_bytes < double(MOE_MXFP4_EAGER_MAX_BYTES)) {
+        hipLaunchKernelGGL((k_dispatch_mxfp4<K, kEven, kPacked, true>), grid, block, 0, s, x, n_rows,
+                           h16, top_k, restore, q, scales, limit, rs);
+        return hipGetLastError();
+      }
+    }
+    hipLaunchKernelGGL((k_dispatch_mxfp4<K, kEven, kPacked, false>), grid, block, 0, s, x, n_rows, h16,
+                       top_k, restore, q, scales, limit, rs);
     return hipGetLastError();
   }
   static hipError_t run(const u32x4* x, int64_t n_rows, int h16, int top_k, const uint32_t* restore,
