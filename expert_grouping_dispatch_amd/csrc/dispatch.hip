@@ -37,12 +37,16 @@ namespace {
 #ifndef MOE_MXFP4_PACKED_NT_STORE
 #define MOE_MXFP4_PACKED_NT_STORE 0
 #endif
-// Outputs (payload and scales) under this size, with top_k <= 8, load each
-// lane's first block of x before the token's positions arrive, so that the
-// two loads are in flight together (rows with nothing routed are then read
-// and dropped).  Larger outputs stream through HBM, where the wasted reads
-// and the registers this takes cost more than the overlap saves (measured on
-// MI355X: 3.7% faster on a 125 MB output, 2.5% slower on a 1.9 GB one).
+// Outputs (payload and scales) of [MIN, MAX) bytes, with top_k <= 8, load
+// each lane's first block of x before the token's positions arrive, so that
+// the two loads are in flight together (rows with nothing routed are then
+// read and dropped).  Measured on MI355X: 3.7% faster on a 125 MB output; no
+// faster on 3-30 MB outputs, which would only read more; 2.5% slower on a
+// 1.9 GB one, where the wasted reads and the registers this takes cost more
+// than the overlap saves.
+#ifndef MOE_MXFP4_EAGER_MIN_BYTES
+#define MOE_MXFP4_EAGER_MIN_BYTES (int64_t(64) << 20)
+#endif
 #ifndef MOE_MXFP4_EAGER_MAX_BYTES
 #define MOE_MXFP4_EAGER_MAX_BYTES (int64_t(256) << 20)
 #endif
@@ -337,7 +341,7 @@ struct LaunchMxfp4 {
     const double out_bytes = double(n_rows) * top_k * (h16 / 4) * 17.0;
     const dim3 grid(row_grid(n_rows * rs.split)), block(kMxThreads);
     if constexpr (K > 0) {
-      if (out_bytes < double(MOE_MXFP4_EAGER_MAX_BYTES)) {
+      if (out_bytes >= double(MOE_MXFP4_EAGER_MIN_BYTES) && out_bytes < double(MOE_MXFP4_EAGER_MAX_BYTES)) {
         hipLaunchKernelGGL((k_dispatch_mxfp4<K, kEven, kPacked, true>), grid, block, 0, s, x, n_rows,
                            h16, top_k, restore, q, scales, limit, rs);
         return hipGetLastError();

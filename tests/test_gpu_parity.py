@@ -561,6 +561,31 @@ def test_dispatch_store_regimes(n, k, h):
     np.testing.assert_array_equal(u16(out[:v]), oracle.dispatch(xb, ref["token_expert_order"], k, v))
 
 
+# MXFP4 output sizes (payload and scales, 17 bytes per block) on each side of
+# the eager-load window [64, 256) MiB, k <= 8 (eager and lazy forms) and
+# k > 8: sampled routed rows against the oracle, a quarter of tokens unrouted.
+@pytest.mark.parametrize("n, k, h", [(1500, 8, 7168), (2600, 8, 7168), (9000, 8, 7168), (600, 12, 7168)])
+def test_dispatch_mxfp4_load_regimes(n, k, h):
+    e = 64
+    out_mib = n * k * (h // 32) * 17 / 2 ** 20
+    print(f"[parity] MXFP4 regimes n={n} k={k} h={h} out={out_mib:.0f} MiB", flush=True)
+    g = np.random.default_rng(n + k + h)
+    ids = g.integers(0, e, size=(n, k)).astype(np.int32)
+    ids[g.random(n) < 0.25] = -1
+    ref = oracle.create_indices(ids, e)
+    v = ref["n_routed"]
+    xb = oracle.f32_to_bf16_rne(g.standard_normal((n, h)).astype(np.float32))
+    restore = torch.from_numpy(ref["restore_token_order"].view(np.int32)).to(DEV).view(torch.uint32)
+    q, sc = mod.alloc_dispatch_mxfp4(n * k, h, DEV)
+    mod.moe_dispatch_mxfp4(bf16_from_bits(xb, DEV), k, restore, q, sc)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(min(v, 64)), g.integers(0, v, size=192), [v - 1]]))
+    teo = ref["token_expert_order"]
+    wq, wsc = oracle.dispatch_mxfp4(xb, teo[rows], k, rows.size)
+    np.testing.assert_array_equal(q[rows].cpu().numpy(), wq)
+    np.testing.assert_array_equal(sc[rows].cpu().numpy(), wsc)
+
+
 def test_workspace_reuse_across_shapes():
     """One zero-filled workspace serves calls of different sizes, expert
     counts and id widths in any order: nothing an earlier call left in it is
