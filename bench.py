@@ -36,9 +36,12 @@ def kernel_of_stage(stage: str, w) -> str:
     """Name of the kernel the library launches for a row stage on workload w
     (a label for the roofline line and the profile it is checked against).
     top_k <= 8 takes the loop-free bf16 dispatch; combine takes it too when
-    the routed rows of y are under 1 GiB, whole-row workgroups otherwise."""
+    the routed rows of y are under 1 GiB, whole-row workgroups otherwise;
+    MXFP4 outputs of at least 256 MiB with top_k <= 8 take the
+    four-lanes-per-block kernel."""
     if stage == "dispatch_mxfp4":
-        return "k_dispatch_mxfp4"
+        out_bytes = w.n_rows * w.top_k * (w.hidden // 32) * 17
+        return "k_dispatch_mxfp4_quad" if w.top_k <= 8 and out_bytes >= (256 << 20) else "k_dispatch_mxfp4"
     if w.top_k > 8:
         return "k_dispatch_bf16" if stage == "dispatch_bf16" else "k_combine"
     if stage == "dispatch_bf16":
@@ -71,6 +74,7 @@ def source_digest(kernel: str) -> str:
     of code, not of its comments, marks the counters as stale."""
     csrc = os.path.join(ROOT, "expert_grouping_dispatch_amd", "csrc")
     files = (["combine.hip", "rows.h", "common.h"] if kernel.startswith("k_combine") else
+             ["dispatch_mxfp4.hip", "rows.h", "common.h"] if kernel.startswith("k_dispatch_mxfp4") else
              ["dispatch.hip", "rows.h", "common.h"] if kernel.startswith("k_dispatch") else [])
     hsh = hashlib.sha256()
     for f in files:
@@ -78,6 +82,20 @@ def source_digest(kernel: str) -> str:
             code = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
         code = re.sub(r"//[^\n]*", " ", code)
         hsh.update("".join(code.split()).encode())
+    return hsh.hexdigest()[:16]
+
+
+def library_digest() -> str:
+    """Digest of every library source (comments and whitespace removed), so
+    that a recorded bench line can be matched with the code it measured."""
+    csrc = os.path.join(ROOT, "expert_grouping_dispatch_amd", "csrc")
+    hsh = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+                code = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
+            code = re.sub(r"//[^\n]*", " ", code)
+            hsh.update(f.encode() + b"\0" + "".join(code.split()).encode())
     return hsh.hexdigest()[:16]
 
 
@@ -172,6 +190,7 @@ def parity_sample(oracle, torch, w, ids, wts, x, y, gpu, n_tok: int = 48):
     want = oracle.combine(ys, wts[toks], mini.reshape(-1), k)
     got = u16(gpu["comb"][torch.from_numpy(toks).to(x.device)])
     ok["combine"] = bool(np.array_equal(got, want))
+    ok["index_error_word_clear"] = int(idx["workspace"][:4].view(torch.int32).item()) == 0
     ok["tokens_sampled"] = int(len(toks))
     ok["all"] = all(v for key, v in ok.items() if key != "tokens_sampled")
     return ok
@@ -494,6 +513,7 @@ def main():
         "frac_of_copy_ceiling": None if copy_gbps is None else round(gbps / copy_gbps, 4),
         "stages": stages, "pipelines": pipelines, "graph_replay": bool(args.graph),
         "extensions": extensions, "roofline": roofline, "cpu_baseline": cpu,
+        "library_digest": library_digest(),
     }
     print(json.dumps(out), flush=True)
 

@@ -27,7 +27,7 @@ __all__ = [
     "moe_mask_padding", "moe_create_indices", "moe_create_indices_workspace_bytes", "moe_mask_create_indices",
     "moe_dispatch", "moe_dispatch_mxfp4", "moe_combine", "moe_combine_epilogue", "moe_error_string",
     "MXFP4_EVEN_SCALE", "MXFP4_PACKED_ROWS",
-    "alloc_indices", "alloc_dispatch", "alloc_dispatch_mxfp4",
+    "alloc_indices", "alloc_dispatch", "alloc_dispatch_mxfp4", "index_workspace_error",
 ]
 
 SENTINEL = 0xFFFFFFFF
@@ -129,6 +129,19 @@ def moe_mask_padding(routing_map: torch.Tensor, real_token_count: torch.Tensor, 
 
 def moe_create_indices_workspace_bytes(n_slots: int, n_experts: int) -> int:
     return int(lib.moe_create_indices_workspace_bytes(int(n_slots), int(n_experts)))
+
+
+def index_workspace_error(workspace: torch.Tensor) -> int:
+    """The sticky error word of an index workspace (its first 32-bit word):
+    bit 0 is set if a cross-workgroup wait of moe_create_indices gave up,
+    bit 1 if a call found the workspace not in the state a zero-filled one is
+    left in.  0 after correct use.  Copies four bytes to the host, so it
+    waits for the work queued on the workspace: not for use under graph
+    capture."""
+    _need(workspace, "workspace", torch.uint8, workspace.device)
+    if workspace.numel() < 4:
+        raise ValueError("workspace is smaller than its error word")
+    return int(workspace[:4].view(torch.int32).item()) & 0xFFFFFFFF
 
 
 def alloc_indices(n_slots: int, n_experts: int, device, scales_offset: bool = False) -> dict:

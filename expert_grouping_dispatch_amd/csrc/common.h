@@ -60,6 +60,18 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
   return v;
 }
 
+// DPP quad_perm moves: lanes (0,1,2,3) of each group of four read lanes
+// (1,0,3,2), or (2,3,0,1).
+constexpr int kDppQuadSwap1 = 0xB1, kDppQuadSwap2 = 0x4E;
+
+// Largest value over each group of four consecutive lanes, returned to all
+// four.  All four lanes must be active.
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+  v = max(v, dpp<kDppQuadSwap1, 0xF>(v));
+  v = max(v, dpp<kDppQuadSwap2, 0xF>(v));
+  return v;
+}
+
 // Largest value over the wave, returned to every lane.
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
   v = max(v, dpp<kDppRowShr1, 0xF>(v));

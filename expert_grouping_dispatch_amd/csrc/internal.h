@@ -44,6 +44,20 @@ constexpr int64_t kIdxChunk = int64_t(kIdxThreads) * kIdxRounds;
 #endif
 constexpr int64_t kIdxSumMaxChunks = MOE_IDX_SUM_MAX_CHUNKS;
 constexpr int64_t kIdxSumMaxEntries = MOE_IDX_SUM_MAX_ENTRIES;
+// Invariants the index kernels rely on, so that a sweep build with other
+// values fails to compile instead of producing wrong indices:
+//  - whole waves, at most 1024 lanes;
+//  - the count table's rows hold 16-bit counts, so a chunk has at most 65535
+//    slots (both chunk sizes);
+//  - the table sums give each 16-byte column of a row (up to 129 of them at
+//    1025 buckets, rounded up to whole waves: 192 lanes) at least one slice
+//    of lanes.
+static_assert(kIdxThreads % 64 == 0 && kIdxThreads <= 1024, "index workgroups are whole waves, at most 1024 lanes");
+static_assert(kIdxRounds >= 1 && kIdxSmallRounds >= 1, "at least one round per chunk");
+static_assert(kIdxChunk <= 65535 && int64_t(kIdxThreads) * kIdxSmallRounds <= 65535,
+              "16-bit per-chunk counts");
+static_assert(kIdxThreads >= (((MOE_MAX_BUCKETS + 7) / 8 + 63) / 64) * 64,
+              "one slice of lanes per count-table column at the largest expert count");
 
 // The caller zero-fills the workspace once.  The kernels keep it ready for
 // the next call of any shape: the last ticket holder resets the ticket, and

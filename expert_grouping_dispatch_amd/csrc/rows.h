@@ -49,6 +49,36 @@ inline uint32_t position_limit(int64_t rows) {
   return rows >= int64_t(0xFFFFFFFFu) ? 0xFFFFFFFFu : uint32_t(rows);
 }
 
+// 16-byte loads and stores, non-temporal (streaming) or plain.
+template <bool kNonTemporal>
+__device__ __forceinline__ u32x4 load_vec(const u32x4* p) {
+  if constexpr (kNonTemporal) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <bool kNonTemporal>
+__device__ __forceinline__ void store_vec(u32x4* p, const u32x4& v) {
+  if constexpr (kNonTemporal) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+// Host: Launch<K>::run(args...) with K = top_k for top_k <= 8 (positions in
+// scalar registers), K = 0 (an LDS list) otherwise.
+template <template <int> class Launch, typename... Args>
+hipError_t by_top_k(int top_k, Args... args) {
+  switch (top_k) {
+    case 1: return Launch<1>::run(args...);
+    case 2: return Launch<2>::run(args...);
+    case 3: return Launch<3>::run(args...);
+    case 4: return Launch<4>::run(args...);
+    case 5: return Launch<5>::run(args...);
+    case 6: return Launch<6>::run(args...);
+    case 7: return Launch<7>::run(args...);
+    case 8: return Launch<8>::run(args...);
+    default: return Launch<0>::run(args...);
+  }
+}
+
 // Positions restore[t*K + j] (and weights) for a compile-time K: the
 // addresses are uniform across the workgroup, so every wave holds them in
 // scalar registers and no LDS or barrier is needed.  Positions >= limit

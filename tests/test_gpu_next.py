@@ -7,6 +7,7 @@ import torch
 
 import oracle
 import workloads
+from tests import _oracle_threads as oracle_threads
 from tests.gpu_common import SENT, bf16_from_bits, check_indices, gpu_available, i32, u16, u32
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -142,6 +143,39 @@ def test_mxfp4_every_finite_value_under_every_scale(flags):
     _mxfp4_case(xb, ids, 1, 1, flags)
 
 
+@pytest.mark.parametrize("flags", [0, 1, 2, 3])
+def test_mxfp4_every_finite_value_wide_output(flags):
+    """The four-lanes-per-block MXFP4 kernel (outputs of 256 MiB or more with
+    top_k <= 8): every finite bf16 value under every block scale, in both
+    scale modes and both layouts, bit-exact against the oracle.  8000 tokens
+    tile the distinct rows of the exhaustive blocks, and each token goes to
+    all 8 experts (in a seeded order), so every row is written 8 times."""
+    even, packed = bool(flags & mod.MXFP4_EVEN_SCALE), bool(flags & mod.MXFP4_PACKED_ROWS)
+    xu = _every_finite_blocks(7 + int(even), 8192)
+    n, k, e, h = 8000, 8, 8, 8192
+    assert n * k * (h // 32) * 17 >= 256 << 20
+    print(f"[parity] MXFP4 wide output, every finite value, flags={flags}", flush=True)
+    x = bf16_from_bits(xu[np.arange(n) % xu.shape[0]], DEV)
+    g = np.random.default_rng(300 + flags)
+    ids = np.argsort(g.random((n, e)), axis=1)[:, :k].astype(np.int32)
+    ref = oracle.create_indices(ids, e)
+    v = ref["n_routed"]
+    restore = torch.from_numpy(ref["restore_token_order"].view(np.int32)).to(DEV).view(torch.uint32)
+    q, sc = mod.alloc_dispatch_mxfp4(n * k, h, DEV, packed=packed)
+    mod.moe_dispatch_mxfp4(x, k, restore, q, sc, flags=flags)
+    torch.cuda.synchronize()
+    pq, ps = oracle_threads.mxfp4_quantize_rows(xu, even)
+    want = torch.from_numpy(np.concatenate([pq, ps], axis=1) if packed else pq).to(DEV)
+    want_s = None if packed else torch.from_numpy(ps).to(DEV)
+    src = torch.from_numpy((ref["token_expert_order"][:v].astype(np.int64) // k) % xu.shape[0]).to(DEV)
+    block = 16384
+    for p0 in range(0, v, block):
+        sl = slice(p0, min(v, p0 + block))
+        assert torch.equal(q[sl], want[src[sl]]), p0
+        if want_s is not None:
+            assert torch.equal(sc[sl], want_s[src[sl]]), p0
+
+
 def test_mxfp4_packed_full_size_sampled():
     """The outlier workload in even + packed mode, checked on sampled rows."""
     w = workloads.WORKLOADS[2]
@@ -260,7 +294,7 @@ def _check_fused(ids, real, tp_rank, e, align=None):
     check_indices(idx, ref)
     if align is not None:
         np.testing.assert_array_equal(u32(idx["scales_offset"]), ref["scales_offset"])
-    assert int(idx["workspace"][:4].view(torch.int32).item()) == 0
+    assert mod.index_workspace_error(idx["workspace"]) == 0
 
 
 @pytest.mark.parametrize("cfg", range(len(workloads.WORKLOADS)))

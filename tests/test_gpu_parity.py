@@ -4,12 +4,15 @@ Bit-exact on the masked routing map, every index output, bf16 dispatch rows
 and MXFP4 payload / scale bytes; combine within 1 bf16 ulp (and bit-exact
 in practice: the kernel does the same fp32 operations in the same order).
 """
+import concurrent.futures as cf
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import workloads
+from tests import _oracle_threads as oracle_threads
 from tests.gpu_common import (SENT, bf16_from_bits, bf16_ulp_distance, check_indices, gpu_available, i32,
                               run_path, u16, u32)
 
@@ -108,47 +111,101 @@ def test_workload_full_size_sampled(cfg):
 
 
 @pytest.mark.parametrize("cfg", [2, 4])
-def test_workload_full_size_every_row(cfg):
-    """Full-size workloads, every routed row, against definitions evaluated on
-    the GPU with plain torch operations (the positions come from the oracle):
-    bf16 dispatch row p is x[teo[p] // k]; the MXFP4 bytes of all k copies of
-    a token are identical (the rows themselves are pinned to the oracle on
-    samples); combine equals fp32 products and sums, each rounded on its own,
-    j ascending, unrouted j skipped, then bf16 round-to-nearest-even."""
+def test_workload_full_size_every_row_bf16(cfg):
+    """Full-size workloads, every routed bf16 dispatch row: row p is
+    x[teo[p] // k] (the oracle's dispatch, a row gather, evaluated on the GPU
+    with the oracle's token_expert_order)."""
     w = workloads.WORKLOADS[cfg]
     ids, wts, real = workloads.make_routing(w, cfg)
-    x, y = workloads.make_dense(w, cfg, DEV)
-    res = run_path(mod, ids, real, w.n_experts, x, y, wts, ("bf16", "mxfp4"))
+    x, _ = workloads.make_dense(w, cfg, DEV, y_rows=1)
+    print(f"[parity] workload {w.name} full size, every bf16 row", flush=True)
+    res = run_path(mod, ids, real, w.n_experts, x, None, wts, ("bf16",))
     _, ref = _oracle_front(ids, real, w.n_experts)
-    n, k, v = w.n_rows, w.top_k, ref["n_routed"]
+    check_indices(res, ref)
+    k, v = w.top_k, ref["n_routed"]
     teo = torch.from_numpy(ref["token_expert_order"][:v].astype(np.int64)).to(DEV)
-    rest = torch.from_numpy(ref["restore_token_order"].astype(np.int64)).to(DEV).view(n, k)
-    block = 4096
-    for p0 in range(0, v, block * 8):
-        sl = slice(p0, min(v, p0 + block * 8))
+    block = 32768
+    for p0 in range(0, v, block):
+        sl = slice(p0, min(v, p0 + block))
         assert torch.equal(res["dispatch"][sl].view(torch.int16), x[teo[sl] // k].view(torch.int16)), p0
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_workload_full_size_every_row_mxfp4(cfg):
+    """Full-size workloads, every routed MXFP4 row (payload and scale bytes)
+    against the oracle: each real token is quantized once by
+    oracle.mxfp4_quantize (row chunks on host threads) and compared with the
+    rows at each of its routed positions.  deepseek_v3_prefill (125 MB of
+    output) runs the eager one-lane-per-block kernel, the stress workload
+    (1.9 GB) the four-lanes-per-block kernel."""
+    w = workloads.WORKLOADS[cfg]
+    ids, wts, real = workloads.make_routing(w, cfg)
+    x, _ = workloads.make_dense(w, cfg, DEV, y_rows=1)
+    print(f"[parity] workload {w.name} full size, every MXFP4 row", flush=True)
+    res = run_path(mod, ids, real, w.n_experts, x, None, wts, ("mxfp4",))
+    _, ref = _oracle_front(ids, real, w.n_experts)
+    check_indices(res, ref)
+    n, k = w.n_rows, w.top_k
+    # every routed slot belongs to a real token (padding rows are masked)
+    assert np.all(ref["restore_token_order"].reshape(n, k)[real:] == SENT)
+    wq, wsc = oracle_threads.mxfp4_quantize_rows(u16(x[:real]))
+    rest = torch.from_numpy(ref["restore_token_order"].astype(np.int64)).to(DEV).view(n, k)
     sent = torch.tensor(SENT, dtype=torch.int64, device=DEV)
-    routed = rest != sent
+    block = 4096
     for t0 in range(0, real, block):
         t1 = min(real, t0 + block)
         r = rest[t0:t1]
-        first = r[:, 0]
-        for j in range(1, k):
-            ok = routed[t0:t1, j] & routed[t0:t1, 0]
-            a, b = r[:, j][ok], first[ok]
-            assert torch.equal(res["q"][a], res["q"][b]) and torch.equal(res["scales"][a], res["scales"][b])
-    wt = torch.from_numpy(wts).to(DEV)
-    for t0 in range(0, n, block):
+        routed = r != sent
+        tok = torch.arange(t1 - t0, device=DEV).view(-1, 1).expand(-1, k)[routed]
+        pos = r[routed]
+        eq = torch.from_numpy(wq[t0:t1]).to(DEV)
+        es = torch.from_numpy(wsc[t0:t1]).to(DEV)
+        assert torch.equal(res["q"][pos], eq[tok]), t0
+        assert torch.equal(res["scales"][pos], es[tok]), t0
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_workload_full_size_every_row_combine(cfg):
+    """Full-size workloads, every combine output row against oracle.combine:
+    the y rows each chunk of tokens reads are gathered on the GPU at the
+    oracle's positions, and the oracle runs on them chunk by chunk on host
+    threads (rows with nothing routed included: they come out +0).  The
+    stress workload runs the whole-row combine kernel, deepseek_v3_prefill
+    the loop-free one."""
+    w = workloads.WORKLOADS[cfg]
+    ids, wts, real = workloads.make_routing(w, cfg)
+    x, y = workloads.make_dense(w, cfg, DEV)
+    print(f"[parity] workload {w.name} full size, every combine row", flush=True)
+    res = run_path(mod, ids, real, w.n_experts, x, y, wts, ())
+    _, ref = _oracle_front(ids, real, w.n_experts)
+    check_indices(res, ref)
+    n, k = w.n_rows, w.top_k
+    rest = ref["restore_token_order"].reshape(n, k)
+    got = res["combine"]
+    block = 2048
+
+    def one(t0):
         t1 = min(n, t0 + block)
-        acc = torch.zeros((t1 - t0, w.hidden), dtype=torch.float32, device=DEV)
-        for j in range(k):
-            rj = rest[t0:t1, j]
-            ok = rj != sent
-            yj = y[torch.where(ok, rj, torch.zeros_like(rj))].float()
-            prod = wt[t0:t1, j:j + 1] * yj
-            acc = torch.where(ok[:, None], acc + prod, acc)
-        want = acc.to(torch.bfloat16).view(torch.int16)
-        assert torch.equal(res["combine"][t0:t1].view(torch.int16), want), t0
+        rs = rest[t0:t1]
+        routed = rs != SENT
+        mini = np.full(rs.shape, SENT, np.uint32)
+        mini[routed] = np.arange(int(routed.sum()), dtype=np.uint32)   # row order of the gathered rows
+        want = oracle.combine(gathered[t0], wts[t0:t1], mini.reshape(-1), k)
+        return t0, want
+
+    gathered = {}
+    with cf.ThreadPoolExecutor(oracle_threads.n_threads()) as ex:
+        futs = []
+        for t0 in range(0, n, block):
+            rs = rest[t0:min(n, t0 + block)]
+            used = rs[rs != SENT].astype(np.int64)
+            gathered[t0] = u16(y[torch.from_numpy(used).to(DEV)]) if used.size else np.zeros((0, w.hidden), np.uint16)
+            futs.append(ex.submit(one, t0))
+        for f in futs:
+            t0, want = f.result()
+            t1 = t0 + want.shape[0]
+            _check_combine(u16(got[t0:t1]), want)
+            del gathered[t0]
 
 
 # ---------------------------------------------------------------- edge cases
@@ -341,7 +398,7 @@ def test_deterministic_under_skew():
 def test_index_error_word_clear(n, e):
     ids, w, real, x, y = _rand_case(40, n, 8, e, 32, "distinct")
     res = run_path(mod, ids, real, e, x, y, w, ("bf16",))
-    assert int(res["workspace"][:4].view(torch.int32).item()) == 0
+    assert mod.index_workspace_error(res["workspace"]) == 0
 
 
 # The multi-chunk index paths: up to 512 chunks whose count table (chunks x
@@ -367,7 +424,7 @@ def test_index_paths_around_the_table_limit(s, e):
     ref = oracle.create_indices(ids, e, scales_align=64)
     check_indices(idx, ref)
     np.testing.assert_array_equal(u32(idx["scales_offset"]), ref["scales_offset"])
-    assert int(idx["workspace"][:4].view(torch.int32).item()) == 0
+    assert mod.index_workspace_error(idx["workspace"]) == 0
     # the one-call mask + indices, masking the last 1000 rows, in the same workspace
     real = s - 1000
     d = torch.from_numpy(ids.reshape(-1)).to(DEV)
@@ -456,6 +513,7 @@ def test_graph_replay_with_device_count(fused, n, k):
         np.testing.assert_array_equal(q[:vq].cpu().numpy(), wq)
         np.testing.assert_array_equal(sc[:vq].cpu().numpy(), wsc)
         _check_combine(u16(comb), oracle.combine(u16(y), w, ref["restore_token_order"], k))
+        assert mod.index_workspace_error(idx["workspace"]) == 0, real
 
 
 @pytest.mark.parametrize("S, E", [((1 << 31) + 4099, 1024), (0xFFFFFFFE, 256)])
@@ -473,7 +531,7 @@ def test_indices_beyond_int32_slots(S, E):
                            idx["restore_token_order"], idx["expert_ids"], idx["expert_usage_stats"],
                            idx["workspace"])
     torch.cuda.synchronize()
-    assert int(idx["workspace"][:4].view(torch.int32).item()) == 0
+    assert mod.index_workspace_error(idx["workspace"]) == 0
 
     def as_i64(t):
         return t.view(torch.int32).to(torch.int64) & 0xFFFFFFFF
@@ -608,7 +666,7 @@ def test_workspace_reuse_across_shapes():
                                idx["restore_token_order"], idx["expert_ids"], idx["expert_usage_stats"], ws)
         torch.cuda.synchronize()
         check_indices(idx, oracle.create_indices(ids, e))
-        assert int(ws[:4].view(torch.int32).item()) == 0, (i, n, k, e)
+        assert mod.index_workspace_error(ws) == 0, (i, n, k, e)
 
 
 def test_concurrent_streams_with_separate_workspaces():
@@ -642,6 +700,7 @@ def test_concurrent_streams_with_separate_workspaces():
             np.testing.assert_array_equal(res["q"][:v].cpu().numpy(), wq)
             np.testing.assert_array_equal(res["scales"][:v].cpu().numpy(), wsc)
             _check_combine(u16(res["combine"]), oracle.combine(u16(y), w, ref["restore_token_order"], k))
+            assert mod.index_workspace_error(res["workspace"]) == 0
     assert len(results) == 2
 
 
@@ -710,7 +769,7 @@ def test_workspace_not_zero_filled_sets_error_word():
     ws[:8].view(torch.int32)[1] = 3             # ticket word
     mod.moe_create_indices(d_ids, e, teo[:s], esi, rest[:s], eid, stats, ws[:ws_bytes])
     torch.cuda.synchronize()
-    assert int(ws[:4].view(torch.int32).item()) != 0
+    assert mod.index_workspace_error(ws) != 0
     assert bool((teo[s:].view(torch.int32) == canary).all()) and bool((rest[s:].view(torch.int32) == canary).all())
     assert bool((ws[ws_bytes:] == 0xA5).all())
 
