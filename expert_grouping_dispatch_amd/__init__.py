@@ -25,6 +25,7 @@ import torch
 __all__ = [
     "SENTINEL", "MoeError", "LIB_PATH", "lib",
     "moe_mask_padding", "moe_create_indices", "moe_create_indices_workspace_bytes", "moe_mask_create_indices",
+    "moe_create_indices_noalloc", "ERR_SCRATCH_LIMIT",
     "moe_dispatch", "moe_dispatch_mxfp4", "moe_combine", "moe_combine_epilogue", "moe_error_string",
     "MXFP4_EVEN_SCALE", "MXFP4_PACKED_ROWS",
     "alloc_indices", "alloc_dispatch", "alloc_dispatch_mxfp4", "index_workspace_error",
@@ -34,6 +35,7 @@ SENTINEL = 0xFFFFFFFF
 MXFP4_BLOCK = 32
 MXFP4_EVEN_SCALE = 1   # flags bit of moe_dispatch_mxfp4: "even-mode" scale exponent
 MXFP4_PACKED_ROWS = 2  # flags bit of moe_dispatch_mxfp4: payload and scales in one row
+ERR_SCRATCH_LIMIT = 5  # status: input too large for moe_create_indices_noalloc's static scratch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_route.so")
 
 if not os.path.exists(LIB_PATH):
@@ -53,6 +55,8 @@ lib.moe_create_indices_workspace_bytes.restype = _sz
 for _f in (lib.moe_create_indices, lib.moe_create_indices_i64):
     _f.argtypes = [_p, _i64, _i32, _p, _p, _p, _p, _p, _p, _u32, _p, _sz, _p]
     _f.restype = ctypes.c_int
+lib.moe_create_indices_noalloc.argtypes = [_p, _i64, _i32, _p, _p, _p, _p, _p, _p, _u32, _p]
+lib.moe_create_indices_noalloc.restype = ctypes.c_int
 for _f in (lib.moe_mask_create_indices, lib.moe_mask_create_indices_i64):
     _f.argtypes = [_p, _i64, _i32, _p, _i32, _i32, _p, _p, _p, _p, _p, _p, _u32, _p, _sz, _p]
     _f.restype = ctypes.c_int
@@ -180,6 +184,25 @@ def moe_create_indices(topk_ids: torch.Tensor, n_experts: int, token_expert_orde
                   int(scales_align), _ptr(workspace), workspace.numel(), _stream(dev)), "moe_create_indices")
 
 
+def moe_create_indices_noalloc(topk_ids: torch.Tensor, n_experts: int, token_expert_order: torch.Tensor,
+                               expert_start_indices: torch.Tensor, restore_token_order: torch.Tensor,
+                               expert_ids: torch.Tensor, expert_usage_stats: torch.Tensor,
+                               scales_offset: torch.Tensor = None, scales_align: int = 128) -> None:
+    """moe_create_indices with the library's static per-GPU scratch instead of a workspace (nothing is
+    allocated).  Inputs past the scratch raise MoeError with status ERR_SCRATCH_LIMIT; calls on one
+    GPU must not overlap."""
+    dev = _device_of(topk_ids)
+    _need(topk_ids, "topk_ids", torch.int32, dev)
+    s = topk_ids.numel()
+    soff = _index_outputs(dev, s, n_experts, token_expert_order, expert_start_indices, restore_token_order,
+                          expert_ids, expert_usage_stats, None, scales_offset)
+    with torch.cuda.device(dev):
+        _check(lib.moe_create_indices_noalloc(_ptr(topk_ids), s, int(n_experts), _ptr(token_expert_order),
+                                              _ptr(expert_start_indices), _ptr(restore_token_order),
+                                              _ptr(expert_ids), _ptr(expert_usage_stats), soff, int(scales_align),
+                                              _stream(dev)), "moe_create_indices_noalloc")
+
+
 def _index_outputs(dev, s, n_experts, token_expert_order, expert_start_indices, restore_token_order,
                    expert_ids, expert_usage_stats, workspace, scales_offset):
     for name, t, odt, n in (("token_expert_order", token_expert_order, torch.uint32, s),
@@ -190,7 +213,8 @@ def _index_outputs(dev, s, n_experts, token_expert_order, expert_start_indices, 
         _need(t, name, odt, dev)
         if t.numel() != n:
             raise ValueError(f"{name} must have {n} elements, has {t.numel()}")
-    _need(workspace, "workspace", torch.uint8, dev)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, dev)
     if scales_offset is None:
         return ctypes.c_void_p(0)
     _need(scales_offset, "scales_offset", torch.uint32, dev)

@@ -3,6 +3,7 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "internal.h"
 #include "moe_route.h"
@@ -55,16 +56,16 @@ int mask_padding(IdT* routing_map, int64_t n_rows, int32_t top_k, const int32_t*
                                            static_cast<hipStream_t>(stream)));
 }
 
+// The argument checks of the index entry points, workspace aside.
 template <typename IdT>
-int create_indices(const IdT* topk_ids, int64_t n_slots, int32_t n_experts,
-                   uint32_t* token_expert_order, uint32_t* expert_start_indices,
-                   uint32_t* restore_token_order, int32_t* expert_ids,
-                   uint32_t* expert_usage_stats, uint32_t* scales_offset, uint32_t scales_align,
-                   void* workspace, size_t workspace_bytes, moe::PadMask pad, void* stream) {
+int index_arguments(const IdT* topk_ids, int64_t n_slots, int32_t n_experts,
+                    const uint32_t* token_expert_order, const uint32_t* expert_start_indices,
+                    const uint32_t* restore_token_order, const int32_t* expert_ids,
+                    const uint32_t* expert_usage_stats, const uint32_t* scales_offset,
+                    uint32_t scales_align) {
   if (n_slots < 0 || n_slots > int64_t(0xFFFFFFFEu) || n_experts < 1 || n_experts > MOE_MAX_EXPERTS)
     return MOE_ERR_INVALID_ARGUMENT;
-  if (expert_start_indices == nullptr || expert_ids == nullptr || expert_usage_stats == nullptr ||
-      workspace == nullptr)
+  if (expert_start_indices == nullptr || expert_ids == nullptr || expert_usage_stats == nullptr)
     return MOE_ERR_INVALID_ARGUMENT;
   if (n_slots > 0 && (topk_ids == nullptr || token_expert_order == nullptr ||
                       restore_token_order == nullptr))
@@ -74,9 +75,22 @@ int create_indices(const IdT* topk_ids, int64_t n_slots, int32_t n_experts,
     return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(topk_ids, sizeof(IdT)) || !aligned(token_expert_order, 4) ||
       !aligned(expert_start_indices, 4) || !aligned(restore_token_order, 4) ||
-      !aligned(expert_ids, 4) || !aligned(expert_usage_stats, 4) || !aligned(scales_offset, 4) ||
-      !aligned(workspace, 256))
+      !aligned(expert_ids, 4) || !aligned(expert_usage_stats, 4) || !aligned(scales_offset, 4))
     return MOE_ERR_INVALID_ARGUMENT;
+  return MOE_OK;
+}
+
+template <typename IdT>
+int create_indices(const IdT* topk_ids, int64_t n_slots, int32_t n_experts,
+                   uint32_t* token_expert_order, uint32_t* expert_start_indices,
+                   uint32_t* restore_token_order, int32_t* expert_ids,
+                   uint32_t* expert_usage_stats, uint32_t* scales_offset, uint32_t scales_align,
+                   void* workspace, size_t workspace_bytes, moe::PadMask pad, void* stream) {
+  if (const int a = index_arguments(topk_ids, n_slots, n_experts, token_expert_order, expert_start_indices,
+                                    restore_token_order, expert_ids, expert_usage_stats, scales_offset,
+                                    scales_align))
+    return a;
+  if (workspace == nullptr || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < moe::index_workspace_bytes(n_slots, n_experts))
     return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (const int d = check_device()) return d;
@@ -104,6 +118,36 @@ int mask_create_indices(IdT* routing_map, int64_t n_rows, int32_t top_k,
                              expert_usage_stats, scales_offset, scales_align, workspace,
                              workspace_bytes, moe::PadMask{real_token_count, top_k, tp_rank},
                              stream);
+}
+
+// ---- scratch of moe_create_indices_noalloc --------------------------------
+// For callers that cannot allocate, the index stage's scratch is this
+// file-scope device array instead of a caller's workspace: one copy per GPU,
+// held from the library's load until the process ends.  Its size is the
+// fixed part of the index workspace, which is all that inputs taking the
+// one-workgroup or the count-table path use; those paths rewrite everything
+// they read from it within the call, so nothing in it needs clearing between
+// calls.  In host code the array's name stands for a host-side shadow:
+// kernels get only the device address looked up below.
+constexpr size_t kScratchBytes = moe::kIndexWorkspaceFixedBytes;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device
+
+// The device address of `scratch` on device `dev` (the current device), looked
+// up on the first call on that device and kept; nullptr if the lookup fails.
+void* scratch_address(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
 }
 
 int combine(const uint16_t* y, int64_t y_rows, const float* router_weights,
@@ -141,6 +185,8 @@ const char* moe_error_string(int status) {
     case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case MOE_ERR_UNSUPPORTED_DEVICE: return "unsupported device (gfx950 required)";
     case MOE_ERR_LAUNCH: return "kernel launch failed";
+    case MOE_ERR_SCRATCH_LIMIT:
+      return "input too large for the static scratch of moe_create_indices_noalloc (needs the lookback path)";
     default: return "unknown status";
   }
 }
@@ -171,6 +217,27 @@ int moe_create_indices(const int32_t* topk_ids, int64_t n_slots, int32_t n_exper
                         restore_token_order, expert_ids, expert_usage_stats, scales_offset,
                         scales_align, workspace, workspace_bytes, moe::PadMask{nullptr, 1, 0},
                         stream);
+}
+
+int moe_create_indices_noalloc(const int32_t* topk_ids, int64_t n_slots, int32_t n_experts,
+                               uint32_t* token_expert_order, uint32_t* expert_start_indices,
+                               uint32_t* restore_token_order, int32_t* expert_ids,
+                               uint32_t* expert_usage_stats, uint32_t* scales_offset,
+                               uint32_t scales_align, void* stream) {
+  if (const int a = index_arguments(topk_ids, n_slots, n_experts, token_expert_order, expert_start_indices,
+                                    restore_token_order, expert_ids, expert_usage_stats, scales_offset,
+                                    scales_align))
+    return a;
+  if (moe::index_workspace_bytes(n_slots, n_experts) > kScratchBytes) return MOE_ERR_SCRATCH_LIMIT;
+  if (const int d = check_device()) return d;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_LAUNCH;
+  void* ws = scratch_address(dev);
+  if (ws == nullptr) return MOE_ERR_LAUNCH;
+  return launched(moe::launch_create_indices(topk_ids, n_slots, n_experts, token_expert_order,
+                                             expert_start_indices, restore_token_order, expert_ids,
+                                             expert_usage_stats, scales_offset, scales_align, ws,
+                                             moe::PadMask{nullptr, 1, 0}, static_cast<hipStream_t>(stream)));
 }
 
 int moe_create_indices_i64(const int64_t* topk_ids, int64_t n_slots, int32_t n_experts,

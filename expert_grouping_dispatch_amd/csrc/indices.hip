@@ -590,14 +590,6 @@ bool index_sum_path(int64_t n_slots, int n_experts) {
   return chunks > 1 && chunks <= kIdxSumMaxChunks && chunks * row <= kIdxSumMaxEntries;
 }
 
-// Fixed layout for every shape: header words, bucket starts for the largest
-// expert count, the count table of the wait-free path at its largest, then
-// the lookback words [chunks][E+1] of this call.
-constexpr size_t kWsHeader = 256;
-constexpr size_t kWsBase = kWsHeader;
-constexpr size_t kWsCounts = kWsBase + ((size_t(MOE_MAX_BUCKETS) * 4 + 255) & ~size_t(255));
-constexpr size_t kWsFlags = kWsCounts + ((size_t(kIdxSumMaxEntries) * 2 + 255) & ~size_t(255));
-
 // Only the lookback path needs words past the fixed part.  Every input
 // smaller than one that takes the lookback path takes either that path with
 // fewer chunks or no lookback at all, so a workspace sized for some n_slots

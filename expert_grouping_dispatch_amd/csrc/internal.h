@@ -72,6 +72,17 @@ struct IndexWorkspace {
   uint64_t* flags;      // [chunks][E+1] (status << 32 | count) lookback words
 };
 
+// Workspace layout, the same for every shape: header words (error, ticket),
+// bucket starts for the largest expert count, the count table at its
+// largest, then the lookback words of the call.  The fixed part (up to the
+// lookback words) is all that inputs taking the one-workgroup or the
+// count-table path use, and they leave nothing in it that a later call reads.
+constexpr size_t kWsHeader = 256;
+constexpr size_t kWsBase = kWsHeader;
+constexpr size_t kWsCounts = kWsBase + ((size_t(MOE_MAX_BUCKETS) * 4 + 255) & ~size_t(255));
+constexpr size_t kWsFlags = kWsCounts + ((size_t(kIdxSumMaxEntries) * 2 + 255) & ~size_t(255));
+constexpr size_t kIndexWorkspaceFixedBytes = kWsFlags;
+
 int index_rounds(int64_t n_slots);
 int64_t index_chunks(int64_t n_slots);
 bool index_sum_path(int64_t n_slots, int n_experts);

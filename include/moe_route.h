@@ -8,7 +8,8 @@
  *   3. moe_dispatch         -- token rows copied into an expert-contiguous
  *      moe_dispatch_mxfp4      buffer, as bf16 or as MXFP4
  *   4. moe_combine          -- weighted sum of expert outputs back per token
- * plus moe_mask_create_indices, stages 1 and 2 in one call.
+ * plus moe_mask_create_indices, stages 1 and 2 in one call, and
+ * moe_create_indices_noalloc, stage 2 for callers that cannot allocate.
  *
  * Conventions shared by every entry point
  *   - Pointers marked [device] are device (HBM) pointers on the current HIP
@@ -24,12 +25,14 @@
  *     into a HIP graph.
  *   - Calls keep no state between them outside the buffers passed, so calls
  *     on different streams may run at once, except that calls sharing an
- *     index workspace must not overlap.
+ *     index workspace must not overlap, and neither may calls of
+ *     moe_create_indices_noalloc on one GPU (they share its static scratch).
  *   - A slot is the pair (token t, choice j) with flat index i = t*top_k + j.
  *     MOE_SENTINEL (0xFFFFFFFF) marks "no slot / no position".
  *   - Return value: MOE_OK, or an error code with nothing enqueued.  Errors
  *     are argument errors detected on the host (null or misaligned pointer,
- *     size out of range), an undersized workspace, a device that is not
+ *     size out of range), an undersized workspace (or an input too large for
+ *     the static scratch of moe_create_indices_noalloc), a device that is not
  *     gfx950 (rejected, never emulated), or a failed launch.  For tests of
  *     that rejection, the environment variable MOE_ROUTE_ASSUME_ARCH, when
  *     set, stands in for the device's architecture name (read once per
@@ -61,7 +64,8 @@ typedef enum moe_status {
   MOE_ERR_INVALID_ARGUMENT = 1,
   MOE_ERR_WORKSPACE_TOO_SMALL = 2,
   MOE_ERR_UNSUPPORTED_DEVICE = 3,
-  MOE_ERR_LAUNCH = 4
+  MOE_ERR_LAUNCH = 4,
+  MOE_ERR_SCRATCH_LIMIT = 5 /* input larger than moe_create_indices_noalloc's static scratch */
 } moe_status;
 
 /* Static, human-readable text for a status code. [host] */
@@ -157,6 +161,38 @@ int moe_create_indices(const int32_t* topk_ids, int64_t n_slots, int32_t n_exper
                        uint32_t* expert_usage_stats, uint32_t* scales_offset,
                        uint32_t scales_align, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/*
+ * As moe_create_indices, with no workspace argument and no allocation of any
+ * kind: for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  The
+ * index stage's scratch is a static device array of the library, one per
+ * GPU, of 266752 bytes (the fixed part of the workspace), held from the
+ * library's load until the process ends.  Arguments, layouts, results and
+ * the other errors are those of moe_create_indices.
+ *
+ * Limit: the input must take the one-workgroup or the count-table path of
+ * the index stage: n_slots <= 2048, or at most 512 chunks (of 1024 slots up
+ * to 65536 slots, of 2048 slots above) whose count table, with
+ * n_experts + 1 rounded up to a multiple of 8 entries per chunk, holds at
+ * most 131072 entries.  That is up to 1,015,808 slots at n_experts = 256,
+ * 1,048,576 at n_experts <= 255 (for n_experts + 1 <= 256 entries), and
+ * 260,096 at n_experts = 1024.  Larger inputs return MOE_ERR_SCRATCH_LIMIT
+ * with nothing enqueued; moe_create_indices with a workspace takes them.
+ * Those paths leave nothing in the scratch that a later call reads, so
+ * nothing needs clearing between calls.
+ *
+ * All calls on one GPU share its scratch: calls that overlap in time on one
+ * GPU (on different streams, or from different threads) race and give
+ * unspecified results.  The first call on a GPU looks up the scratch's
+ * device address (not a stream operation); if a runtime refuses that lookup
+ * during stream capture, make one call outside capture first.
+ */
+int moe_create_indices_noalloc(const int32_t* topk_ids, int64_t n_slots, int32_t n_experts,
+                               uint32_t* token_expert_order, uint32_t* expert_start_indices,
+                               uint32_t* restore_token_order, int32_t* expert_ids,
+                               uint32_t* expert_usage_stats, uint32_t* scales_offset,
+                               uint32_t scales_align, void* stream);
 
 /* As moe_create_indices for int64 expert ids (topk_ids [n_slots] int64). */
 int moe_create_indices_i64(const int64_t* topk_ids, int64_t n_slots, int32_t n_experts,

@@ -26,6 +26,7 @@ def test_header_declares_the_path():
     assert declared_functions() == sorted([
         "moe_error_string", "moe_mask_padding", "moe_mask_padding_i64", "moe_create_indices_workspace_bytes",
         "moe_create_indices", "moe_create_indices_i64", "moe_mask_create_indices", "moe_mask_create_indices_i64",
+        "moe_create_indices_noalloc",
         "moe_dispatch", "moe_dispatch_mxfp4", "moe_combine", "moe_combine_epilogue"])
 
 
@@ -40,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_error_strings():
     assert mod.moe_error_string(0) == "ok"
-    for s in range(1, 5):
+    for s in range(1, 6):
         assert mod.moe_error_string(s) not in ("ok", "unknown status")
     assert mod.moe_error_string(99) == "unknown status"
 
@@ -104,6 +105,18 @@ def test_invalid_arguments_rejected_on_host():
         assert fn(*bad) == 2                                        # workspace too small
     assert L.moe_mask_create_indices_i64(P(260), 50, 2, cnt, 0, 8, fake, fake, fake, fake, fake, None, 0,
                                          fake, ws, None) == 1       # int64 map misaligned
+    noalloc = [fake, 100, 8, fake, fake, fake, fake, fake, None, 0, None]
+    N = L.moe_create_indices_noalloc
+    bad = list(noalloc); bad[2] = 0
+    assert N(*bad) == 1                                             # n_experts < 1
+    bad = list(noalloc); bad[3] = None
+    assert N(*bad) == 1                                             # null token_expert_order
+    bad = list(noalloc); bad[8] = fake
+    assert N(*bad) == 1                                             # scales_offset with align 0
+    # past the static scratch (the lookback path) -> MOE_ERR_SCRATCH_LIMIT, before any device use
+    for n_slots, e in [(496 * 2048 + 1, 256), (512 * 2048 + 1, 8), (127 * 2048 + 1, 1024), (2 ** 32 - 2, 1)]:
+        bad = list(noalloc); bad[1] = n_slots; bad[2] = e
+        assert N(*bad) == mod.ERR_SCRATCH_LIMIT, (n_slots, e)
     assert L.moe_dispatch(fake, 10, 12, 2, fake, fake, 20, None) == 1        # hidden % 8
     assert L.moe_dispatch(P(258), 10, 16, 2, fake, fake, 20, None) == 1      # misaligned x
     assert L.moe_dispatch(fake, 10, 16, 0, fake, fake, 20, None) == 1        # top_k < 1
@@ -143,6 +156,9 @@ def test_no_device_is_rejected_after_the_argument_checks():
     assert L.moe_dispatch(fake, 10, 16, 2, fake, fake, 20, None) == 3
     assert L.moe_dispatch_mxfp4(fake, 10, 64, 2, fake, fake, fake, 20, 0, None) == 3
     assert L.moe_combine(fake, 20, fake, fake, 10, 16, 2, fake, None) == 3
+    # the largest inputs the static scratch takes reach the device check
+    for n_slots, e in [(100, 8), (496 * 2048, 256), (512 * 2048, 8), (127 * 2048, 1024)]:
+        assert L.moe_create_indices_noalloc(fake, n_slots, e, fake, fake, fake, fake, fake, None, 0, None) == 3
 
 
 def test_workspace_size_follows_the_index_paths():
