@@ -5,7 +5,10 @@
 // kIdxChunk slots, or half that for inputs up to kIdxSmallMaxSlots so that
 // more workgroups share them); for S <= kIdxChunk one workgroup of the
 // fewest whole waves that hold the slots does all three steps in one launch
-// (k_index_one).  More chunks take two launches, one workgroup per chunk:
+// (k_index_one).  With at most 16 experts and few chunks, one launch of one
+// workgroup per chunk (k_index_few) in which every workgroup counts all the
+// slots itself.  Other inputs of more chunks take two launches, one
+// workgroup per chunk:
 //   up to kIdxSumMaxChunks chunks with a count table of at most
 //   kIdxSumMaxEntries entries (every workload here), without waits:
 //     k_index_count        LDS histogram -> one row of 16-bit counts;
@@ -572,6 +575,138 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scatter_sum(
   wave_scatter<false, R, kIdxThreads>(tile, n_experts, off, whist, teo, restore, n_slots);
 }
 
+// Few experts (E <= NB, NB = 8 or 16) and 2 to J chunk rounds: one launch,
+// no workspace.  Every chunk workgroup counts all the slots itself, which
+// must then cost only a few vector instructions per slot: each lane adds
+// 1 << 8e into a 64-bit word per 8 experts (byte e counts expert e), and a
+// wave sums its words once at the end.  Scalar per-expert ballot counts were
+// tried first: the scalar unit, shared by the CU's 16 waves, then bounded the
+// kernel.  Wave w takes round r of chunk q as its group j = q*R + r, so
+// groups j < c*R lie in the chunks before chunk c.  Only routed slots are
+// counted; the unrouted bucket gets what they leave, of all slots (totals)
+// and of the c*R*kIdxThreads slots before the chunk (its offset).  The
+// chunk's own ids are loaded once more in the layout of the scatter, which
+// then follows as in k_index_scatter_sum.  Padding slots (the one-call mask
+// + index) are unrouted everywhere; only the owning chunk writes -1 into
+// them, and the other workgroups, which may read either value, never look
+// at it.  n_slots < 2^31 here, so slot indices are 32-bit.
+template <typename IdT, int R, int NB, int J>
+__global__ __launch_bounds__(kIdxThreads) void k_index_few(
+    const IdT* ids, int64_t n_slots, uint32_t n_experts, int nbits, int n_chunks,
+    uint32_t* __restrict__ esi, int32_t* __restrict__ expert_ids, uint32_t* __restrict__ stats,
+    uint32_t* __restrict__ soff, uint32_t align, uint32_t* __restrict__ teo,
+    uint32_t* __restrict__ restore, PadMask pad, IdT* wmap) {
+  extern __shared__ uint32_t lds[];
+  __shared__ uint32_t wcount[2][kIdxWaves][NB / 2];  // per wave, packed: all slots, slots before the chunk
+  constexpr uint32_t kChunkSlots = uint32_t(R) * kIdxThreads;
+  const int nb = int(n_experts) + 1;
+  const int c = blockIdx.x;
+  const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
+  uint32_t* tot = lds;          // [nb] slots of each bucket in all chunks
+  uint32_t* off = tot + nb;     // [nb] in the chunks before this one, then this chunk's start
+  uint32_t* base = off + nb;    // [nb] bucket starts
+  uint32_t* whist = base + nb;  // [waves][nb]
+  const int64_t pad_from = pad_begin(pad, n_slots);
+  const uint32_t n32 = uint32_t(n_slots), pad32 = uint32_t(pad_from);
+  const int64_t begin = int64_t(c) * kChunkSlots;
+  IdT own[R];
+  wave_load_ids<false>(ids, n_slots, begin, own);
+  // all J groups' loads in flight together, each id reduced to its counted
+  // key at once (an expert, or kSent for the unrouted, padding and past the
+  // last slot) so that 32 groups of 64-bit ids need no more registers than
+  // 32-bit ones; groups past the last slot load the last slot again, in
+  // bounds
+  uint32_t key[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint32_t i = uint32_t(j / R) * kChunkSlots + uint32_t(wave * R + j % R) * kWave + lane;
+    const uint32_t b = bucket_of(ids[i < n32 ? i : n32 - 1], n_experts);
+    key[j] = (i < pad32 && b < n_experts) ? b : kSent;  // pad32 <= n32
+  }
+  const int n_groups = n_chunks * R, g_own = c * R;
+  // per lane, byte e of cnt[h] counts the lane's slots of expert 8h + e (at
+  // most J <= 32 per byte); snap holds the counts of the groups before the
+  // chunk, a prefix of the loop
+  constexpr int H = NB / 8;
+  uint64_t cnt[H] = {}, snap[H] = {};
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (j < n_groups) {  // the same for the whole workgroup
+#pragma unroll
+      for (int h = 0; h < H; ++h) {
+        const uint32_t kh = key[j] - 8u * h;
+        cnt[h] += uint64_t(kh < 8u ? 1u : 0u) << ((kh & 7u) * 8u);
+      }
+      if (j + 1 == g_own) {
+#pragma unroll
+        for (int h = 0; h < H; ++h) snap[h] = cnt[h];
+      }
+    }
+  }
+  // wave sums: even and odd bytes widened to 16-bit fields (a field's sum is
+  // at most 64 * 32), four 32-bit words per 8 experts: word 2p + (e >> 2)
+  // holds expert e of parity p in its half (e >> 1) & 1
+  {
+    uint32_t packed[2][4 * H];
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+#pragma unroll
+      for (int which = 0; which < 2; ++which) {
+        const uint64_t v = which ? snap[h] : cnt[h];
+        const uint64_t ev = v & 0x00FF00FF00FF00FFull, od = (v >> 8) & 0x00FF00FF00FF00FFull;
+        packed[which][4 * h + 0] = uint32_t(ev);
+        packed[which][4 * h + 1] = uint32_t(ev >> 32);
+        packed[which][4 * h + 2] = uint32_t(od);
+        packed[which][4 * h + 3] = uint32_t(od >> 32);
+      }
+    }
+#pragma unroll
+    for (int which = 0; which < 2; ++which)
+#pragma unroll
+      for (int q = 0; q < 4 * H; ++q) {
+        const uint32_t t = wave_inclusive_sum(packed[which][q]);
+        if (lane == kWave - 1) wcount[which][wave][q] = t;
+      }
+  }
+  __syncthreads();
+  // expert b's count from a wave's packed words
+  auto field = [](const uint32_t* words, int b) {
+    const int e = b & 7;
+    return (words[4 * (b >> 3) + 2 * (e & 1) + (e >> 2)] >> (16 * ((e >> 1) & 1))) & 0xFFFFu;
+  };
+  // wave 0: lane b < E sums expert b over the waves; the unrouted bucket
+  // (lane E) is what the wave-wide sums of the routed counts leave
+  if (wave == 0) {
+    uint32_t t = 0, p = 0;
+    if (lane < int(n_experts)) {
+#pragma unroll
+      for (int w = 0; w < kIdxWaves; ++w) {
+        t += field(wcount[0][w], lane);
+        p += field(wcount[1][w], lane);
+      }
+    }
+    const uint32_t rt = __builtin_amdgcn_readlane(wave_inclusive_sum(t), kWave - 1);
+    const uint32_t rp = __builtin_amdgcn_readlane(wave_inclusive_sum(p), kWave - 1);
+    if (lane == int(n_experts)) {
+      t = n32 - rt;
+      p = uint32_t(c) * kChunkSlots - rp;
+    }
+    if (lane < nb) {  // nb <= 17
+      tot[lane] = t;
+      off[lane] = p;
+    }
+  }
+  __syncthreads();
+  finalize_counts<kIdxThreads>(tot, n_experts, base, esi, expert_ids, stats, soff, align, c == 0);
+  WaveTile<R> tile;
+  wave_keys(own, wmap, n_slots, begin, n_experts, tile, pad_from);
+  wave_count_keys(n_experts, nbits, whist, tile);
+  __syncthreads();
+  for (int b = tid; b < nb; b += kIdxThreads) off[b] += base[b];
+  __syncthreads();
+  wave_scatter<false, R, kIdxThreads>(tile, n_experts, off, whist, teo, restore, n_slots);
+}
+
 // Rounds per chunk: up to kIdxChunk slots one workgroup takes them all; up to
 // kIdxSmallMaxSlots, chunks of kIdxSmallRounds rounds put more workgroups on
 // the few chunks there are; larger inputs use kIdxRounds.
@@ -588,6 +723,17 @@ bool index_sum_path(int64_t n_slots, int n_experts) {
   const int64_t chunks = index_chunks(n_slots);
   const int64_t row = (int64_t(n_experts) + 8) & ~int64_t(7);  // E+1 rounded up to a multiple of 8
   return chunks > 1 && chunks <= kIdxSumMaxChunks && chunks * row <= kIdxSumMaxEntries;
+}
+
+// The few-expert pass takes chunks of kIdxSmallRounds rounds only (every
+// input with so few chunks has them unless the build changes the limits), up
+// to kIdxFewMaxGroups groups per wave at 8 experts or fewer and half that at
+// 9 to 16, whose count costs twice as much per slot.
+bool index_few_path(int64_t n_slots, int n_experts) {
+  const int64_t chunks = index_chunks(n_slots);
+  const int64_t max_groups = n_experts <= 8 ? kIdxFewMaxGroups : kIdxFewMaxGroups / 2;
+  return chunks > 1 && n_experts <= kIdxFewMaxExperts && index_rounds(n_slots) == kIdxSmallRounds &&
+         chunks * kIdxSmallRounds <= max_groups;
 }
 
 // Only the lookback path needs words past the fixed part.  Every input
@@ -652,6 +798,40 @@ hipError_t launch_sums(const IdT* ids, int64_t n_slots, int n_experts, int nbits
   return hipGetLastError();
 }
 
+// The one-launch pass for few experts, chunks of R rounds: NB counted
+// buckets (8 or 16) and J groups per wave (8, 16 or 32; 8 or 16 at NB = 16),
+// the fewest that hold the experts and the chunk rounds.
+template <typename IdT, int R, int NB, int J>
+hipError_t launch_few(const IdT* ids, int64_t n_slots, int n_experts, int nbits, int64_t chunks,
+                      uint32_t* esi, int32_t* expert_ids, uint32_t* stats, uint32_t* soff,
+                      uint32_t align, uint32_t* teo, uint32_t* restore, PadMask pad, IdT* wmap,
+                      hipStream_t s) {
+  const size_t lds = size_t(3 + kIdxWaves) * size_t(n_experts + 1) * sizeof(uint32_t);
+  hipLaunchKernelGGL((k_index_few<IdT, R, NB, J>), dim3(uint32_t(chunks)), dim3(kIdxThreads), lds, s,
+                     ids, n_slots, uint32_t(n_experts), nbits, int(chunks), esi, expert_ids, stats,
+                     soff, align, teo, restore, pad, wmap);
+  return hipGetLastError();
+}
+
+template <typename IdT, int R>
+hipError_t launch_few_groups(const IdT* ids, int64_t n_slots, int n_experts, int nbits,
+                             int64_t chunks, uint32_t* esi, int32_t* expert_ids, uint32_t* stats,
+                             uint32_t* soff, uint32_t align, uint32_t* teo, uint32_t* restore,
+                             PadMask pad, IdT* wmap, hipStream_t s) {
+  const int64_t groups = chunks * R;
+#define MOE_INDEX_FEW(NB, J) \
+  launch_few<IdT, R, NB, J>(ids, n_slots, n_experts, nbits, chunks, esi, expert_ids, stats, soff, \
+                            align, teo, restore, pad, wmap, s)
+  if (n_experts <= 8) {
+    if (groups <= 8) return MOE_INDEX_FEW(8, 8);
+    if (groups <= 16) return MOE_INDEX_FEW(8, 16);
+    return MOE_INDEX_FEW(8, 32);
+  }
+  if (groups <= 8) return MOE_INDEX_FEW(16, 8);
+  return MOE_INDEX_FEW(16, 16);  // at most kIdxFewMaxGroups / 2 <= 16 groups
+#undef MOE_INDEX_FEW
+}
+
 // The one-workgroup pass with T lanes.
 template <typename IdT, int T>
 hipError_t launch_one(const IdT* ids, int64_t n_slots, int n_experts, int nbits, uint32_t* esi,
@@ -687,6 +867,10 @@ hipError_t launch_create_indices(const IdT* ids, int64_t n_slots, int n_experts,
     return MOE_INDEX_ONE(kIdxThreads);
 #undef MOE_INDEX_ONE
   }
+  if (index_few_path(n_slots, n_experts))
+    return launch_few_groups<IdT, kIdxSmallRounds>(ids, n_slots, n_experts, nbits, chunks, esi,
+                                                   expert_ids, stats, soff, align, teo, restore,
+                                                   pad, wmap, s);
   if (index_sum_path(n_slots, n_experts)) {
     if (index_rounds(n_slots) == kIdxSmallRounds)
       return launch_sums<IdT, kIdxSmallRounds>(ids, n_slots, n_experts, nbits, chunks, ws, esi,

@@ -42,6 +42,18 @@ constexpr int64_t kIdxChunk = int64_t(kIdxThreads) * kIdxRounds;
 #ifndef MOE_IDX_SUM_MAX_ENTRIES
 #define MOE_IDX_SUM_MAX_ENTRIES (1 << 17)
 #endif
+// Inputs of at most kIdxFewMaxExperts experts and 2 to kIdxFewMaxGroups
+// chunk rounds (chunks x rounds per chunk) take one launch in which every
+// chunk workgroup counts all the slots itself, one ballot per expert
+// (k_index_few).  0 turns that path off.
+#ifndef MOE_IDX_FEW_MAX_GROUPS
+#define MOE_IDX_FEW_MAX_GROUPS 32
+#endif
+#ifndef MOE_IDX_FEW_MAX_EXPERTS
+#define MOE_IDX_FEW_MAX_EXPERTS 16
+#endif
+constexpr int64_t kIdxFewMaxGroups = MOE_IDX_FEW_MAX_GROUPS;
+constexpr int kIdxFewMaxExperts = MOE_IDX_FEW_MAX_EXPERTS;
 constexpr int64_t kIdxSumMaxChunks = MOE_IDX_SUM_MAX_CHUNKS;
 constexpr int64_t kIdxSumMaxEntries = MOE_IDX_SUM_MAX_ENTRIES;
 // Invariants the index kernels rely on, so that a sweep build with other
@@ -58,6 +70,9 @@ static_assert(kIdxChunk <= 65535 && int64_t(kIdxThreads) * kIdxSmallRounds <= 65
               "16-bit per-chunk counts");
 static_assert(kIdxThreads >= (((MOE_MAX_BUCKETS + 7) / 8 + 63) / 64) * 64,
               "one slice of lanes per count-table column at the largest expert count");
+static_assert(kIdxFewMaxGroups >= 0 && kIdxFewMaxGroups <= 32 && kIdxFewMaxExperts >= 1 &&
+                  kIdxFewMaxExperts <= 16,
+              "the few-expert pass holds at most 32 groups of ids and 16 expert counts per wave");
 
 // The caller zero-fills the workspace once.  The kernels keep it ready for
 // the next call of any shape: the last ticket holder resets the ticket, and
@@ -86,6 +101,7 @@ constexpr size_t kIndexWorkspaceFixedBytes = kWsFlags;
 int index_rounds(int64_t n_slots);
 int64_t index_chunks(int64_t n_slots);
 bool index_sum_path(int64_t n_slots, int n_experts);
+bool index_few_path(int64_t n_slots, int n_experts);
 size_t index_workspace_bytes(int64_t n_slots, int n_experts);
 IndexWorkspace index_workspace_carve(void* ws, int64_t n_slots, int n_experts);
 

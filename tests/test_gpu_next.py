@@ -343,6 +343,40 @@ def test_indices_one_workgroup_sizes(s, e):
     _check_fused(ids, s - s // 3, 0, e, 16)
 
 
+# The one-launch few-expert index pass: 2 to 32 chunks of 1024 slots with at
+# most 8 experts, 2 to 16 chunks with 9 to 16 (8 or 16 counted experts; 8, 16
+# or 32 groups per wave), and just past each limit (33 and 17 chunks, 17
+# experts); int32 and int64 maps with unrouted and out-of-range ids; the
+# separate and the one-call forms.
+@pytest.mark.parametrize("s, k, e", [(2049, 1, 1), (2050, 2, 8), (5000, 1, 12), (8199, 1, 8), (16384, 2, 8),
+                                     (16384, 1, 16), (16385, 1, 16), (24000, 3, 9), (32768, 2, 8),
+                                     (32769, 1, 8), (20000, 4, 17)])
+@pytest.mark.parametrize("dtype", [np.int32, np.int64])
+def test_index_few_expert_path(s, k, e, dtype):
+    n = s // k
+    g = np.random.default_rng(s * 31 + e)
+    pool = [-1, -5, e, e + 5] + list(range(e)) * 3
+    if dtype == np.int64:
+        pool += [-(2 ** 40), 2 ** 31, 2 ** 33 + 1]
+    ids = g.choice(np.array(pool, np.int64), size=(n, k)).astype(dtype)
+    print(f"[parity] few-expert indices: S={s} k={k} E={e} {np.dtype(dtype).name}", flush=True)
+    idx = _indices(torch.from_numpy(ids).to(DEV), e, 16)
+    ref = oracle.create_indices(ids, e, scales_align=16)
+    check_indices(idx, ref)
+    np.testing.assert_array_equal(u32(idx["scales_offset"]), ref["scales_offset"])
+    # masking from inside a chunk, and everything masked
+    _check_fused(ids, n - n // 3 - 5, 0, e, 16)
+    _check_fused(ids, 0, 0, e)
+
+
+@pytest.mark.parametrize("s, e", [(32768, 8), (16384, 16)])
+def test_index_few_expert_path_one_expert(s, e):
+    """Every slot on one expert: the largest counts the pass keeps per wave."""
+    ids = np.full((s, 1), e - 1, np.int32)
+    idx = _indices(torch.from_numpy(ids).to(DEV), e)
+    check_indices(idx, oracle.create_indices(ids, e))
+
+
 @pytest.mark.parametrize("align", [1, 128])
 def test_fused_mask_indices_int64_and_offsets(align):
     n, k, e, real = 5000, 8, 256, 4321
