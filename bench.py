@@ -2,9 +2,10 @@
 """Benchmark of the MoE token-routing path on one MI355X.
 
 One step = the whole path over one batch of the chosen workload:
-    moe_mask_padding -> moe_create_indices -> moe_dispatch (bf16)
+    moe_mask_create_indices (mask + indices, one call) -> moe_dispatch (bf16)
     -> moe_dispatch_mxfp4 -> moe_combine
-with inputs resident in HBM.  Prints ONE JSON line on stdout (progress goes
+with inputs resident in HBM.  Stage times also cover moe_mask_padding and
+moe_create_indices as separate calls.  Prints ONE JSON line on stdout (progress goes
 to stderr).  `value` = routed token-slots per second of the whole step.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
@@ -238,22 +239,19 @@ def time_extensions(torch, moe, w, x, y, d_ids, d_w, idx, n_routed, reps):
     return res
 
 
-def time_pipelines(torch, calls, bts, n_routed, steps, warmup, scrub=None, fused_front=None):
-    """Each single-format pipeline (mask -> indices -> one dispatch -> combine)
-    run as its own loop of `steps` passes, events around each pass (and
-    around every stage in a second loop, for the stage times).  A
-    stage's writes can still be draining from the memory-side cache when the
-    next kernel starts, so only a pipeline's own loop charges it what it
-    leaves behind.  With fused_front (the one-call mask + indices), the two
-    pipelines are also timed with it in place of the first two calls."""
+def time_pipelines(torch, calls, bts, n_routed, steps, warmup, scrub, fused_front):
+    """Each single-format pipeline (the one-call mask + indices -> one
+    dispatch -> combine) run as its own loop of `steps` passes, events around
+    each pass (and around every stage in a second loop, for the stage times).
+    A stage's writes can still be draining from the memory-side cache when
+    the next kernel starts, so only a pipeline's own loop charges it what it
+    leaves behind.  The *_separate_front lines take the mask and the indices
+    as two calls (calls[0], calls[1]) instead."""
     res = {}
-    plans = [("bf16", [(STAGES[j], calls[j]) for j in (0, 1, 2, 4)]),
-             ("mxfp4", [(STAGES[j], calls[j]) for j in (0, 1, 3, 4)])]
-    if fused_front is not None:
-        plans += [("bf16_fused_front", [("mask_indices", fused_front), ("dispatch_bf16", calls[2]),
-                                        ("combine", calls[4])]),
-                  ("mxfp4_fused_front", [("mask_indices", fused_front), ("dispatch_mxfp4", calls[3]),
-                                         ("combine", calls[4])])]
+    plans = [("bf16", [("mask_indices", fused_front), ("dispatch_bf16", calls[2]), ("combine", calls[4])]),
+             ("mxfp4", [("mask_indices", fused_front), ("dispatch_mxfp4", calls[3]), ("combine", calls[4])]),
+             ("bf16_separate_front", [(STAGES[j], calls[j]) for j in (0, 1, 2, 4)]),
+             ("mxfp4_separate_front", [(STAGES[j], calls[j]) for j in (0, 1, 3, 4)])]
     bts = dict(bts, mask_indices=bts["mask"] + bts["indices"])
     for pname, plan in plans:
         names = [nm for nm, _ in plan]
@@ -394,9 +392,17 @@ def main():
         del a, b
         log("calibration copy of 1073741824 bytes done")
 
-    calls = stage_calls()
+    def fused_front():
+        moe.moe_mask_create_indices(d_ids, d_cnt, 0, e, idx["token_expert_order"], idx["expert_start_indices"],
+                                    idx["restore_token_order"], idx["expert_ids"], idx["expert_usage_stats"],
+                                    idx["workspace"])
+
+    calls = stage_calls()                      # the five entry points one by one (stage times)
+    step_calls = [fused_front] + calls[2:]     # the step: mask + indices in one call
     for _ in range(args.warmup):
         for c in calls:
+            c()
+        for c in step_calls:
             c()
     torch.cuda.synchronize()
     n_routed = int(idx["expert_start_indices"][idx["expert_usage_stats"][1].to(torch.int64)].item()) \
@@ -408,13 +414,13 @@ def main():
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            for c in calls:
+            for c in step_calls:
                 c()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            for c in calls:
+            for c in step_calls:
                 c()
         graph.replay()
         torch.cuda.synchronize()
@@ -432,7 +438,7 @@ def main():
         if graph is not None:
             graph.replay()
         else:
-            for c in calls:
+            for c in step_calls:
                 c()
         ev[i][1].record()
     torch.cuda.synchronize()
@@ -470,12 +476,10 @@ def main():
         if counted is not None:
             stages[name]["counter_bytes"] = counted
             stages[name]["counter_gbps"] = round(counted / (stage_ms[name] * 1e-3) / 1e9, 1)
-    def fused_front():
-        moe.moe_mask_create_indices(d_ids, d_cnt, 0, e, idx["token_expert_order"], idx["expert_start_indices"],
-                                    idx["restore_token_order"], idx["expert_ids"], idx["expert_usage_stats"],
-                                    idx["workspace"])
-
     pipelines = time_pipelines(torch, calls, bts, n_routed, args.steps, args.warmup, scrub, fused_front)
+    mi = pipelines["bf16"]["stage_ms"]["mask_indices"]  # the one-call front, as the step runs it
+    stages["mask_indices"] = {"ms": mi, "bytes": bts["mask"] + bts["indices"],
+                              "gbps": round((bts["mask"] + bts["indices"]) / (mi * 1e-3) / 1e9, 1)}
     for pname, pl in pipelines.items():
         log(f"{pname} pipeline: {pl['ms']:.3f} ms/pass, {pl['gbps']} GB/s ({pl['frac_of_peak'] * 100:.1f}% of peak)")
 
@@ -505,7 +509,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "n_rows": n, "real_token_count": real, "hidden": h, "n_experts": e,
                    "top_k": k, "routing": w.routing,
-                   "step": "mask+create_indices+dispatch_bf16+dispatch_mxfp4+combine"},
+                   "step": "mask_create_indices+dispatch_bf16+dispatch_mxfp4+combine"},
         "gbps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "step_ms_median": round(float(np.median(per_step)), 4), "step_ms_min": round(float(np.min(per_step)), 4),
         "scrub_between_steps": scrub is not None,

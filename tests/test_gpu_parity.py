@@ -453,14 +453,15 @@ def test_argument_errors_on_device():
 
 
 # index paths: count table (8192 slots), one workgroup (2048), lookback (1.12M slots, 547 chunks)
-@pytest.mark.parametrize("fused, n, k", [(False, 2048, 4), (True, 2048, 4), (False, 256, 8), (True, 256, 8),
-                                         (False, 140000, 8), (True, 140000, 8)])
-def test_graph_replay_with_device_count(fused, n, k):
+@pytest.mark.parametrize("fused, n, k, e", [(False, 2048, 4, 64), (True, 2048, 4, 64), (False, 256, 8, 64),
+                                            (True, 256, 8, 64), (False, 140000, 8, 64), (True, 140000, 8, 64),
+                                            (False, 4096, 2, 8), (True, 8192, 2, 8)])   # few-expert pass
+def test_graph_replay_with_device_count(fused, n, k, e):
     """Capture mask+indices+dispatch+combine once (mask and indices as two
     calls, or as the one-call entry point); change only the device-side count
     between replays (with eager work in between) and check each replay.  On
     the large input, MXFP4 rows are checked for the first 4096 positions."""
-    e, h = 64, 64
+    h = 64
     ids0, w, _, x, y = _rand_case(50, n, k, e, h, "distinct")
     d_ids = torch.from_numpy(ids0).to(DEV)
     d_src = d_ids.clone()

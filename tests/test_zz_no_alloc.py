@@ -62,7 +62,8 @@ def _both(ids, e, align=None):
 def test_noalloc_matches_the_workspace_entry_point_on_shrinking_inputs():
     """Three calls in a row, each smaller than the one before: the stress
     workload's shape (524,288 slots, E = 256, 256 count-table chunks, padding
-    rows masked), a mid-size one (16,384 slots, E = 8, 16 chunks) and a
+    rows masked), a mid-size one (16,384 slots, E = 8, 16 chunks, the one-launch
+    few-expert pass, which uses no scratch) and a
     decode-sized one (2,048 slots, E = 256, the one-workgroup pass)."""
     _both(_ids(1, 65536, 8, 256, masked=4096), 256, align=128)
     _both(_ids(2, 8192, 2, 8, masked=1192), 8)
