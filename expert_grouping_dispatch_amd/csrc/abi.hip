@@ -125,9 +125,9 @@ int mask_create_indices(IdT* routing_map, int64_t n_rows, int32_t top_k,
 // file-scope device array instead of a caller's workspace: one copy per GPU,
 // held from the library's load until the process ends.  Its size is the
 // fixed part of the index workspace, which is all that inputs taking the
-// one-workgroup or the count-table path use; those paths rewrite everything
-// they read from it within the call, so nothing in it needs clearing between
-// calls.  In host code the array's name stands for a host-side shadow:
+// one-workgroup, the few-expert (none of it) or the count-table path use;
+// those paths rewrite everything they read from it within the call, so
+// nothing in it needs clearing between calls.  In host code the array's name stands for a host-side shadow:
 // kernels get only the device address looked up below.
 constexpr size_t kScratchBytes = moe::kIndexWorkspaceFixedBytes;
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];

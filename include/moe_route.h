@@ -171,8 +171,9 @@ int moe_create_indices(const int32_t* topk_ids, int64_t n_slots, int32_t n_exper
  * library's load until the process ends.  Arguments, layouts, results and
  * the other errors are those of moe_create_indices.
  *
- * Limit: the input must take the one-workgroup or the count-table path of
- * the index stage: n_slots <= 2048, or at most 512 chunks (of 1024 slots up
+ * Limit: the input must take a path of the index stage that needs no
+ * lookback words (the one-workgroup, few-expert or count-table path):
+ * n_slots <= 2048, or at most 512 chunks (of 1024 slots up
  * to 65536 slots, of 2048 slots above) whose count table, with
  * n_experts + 1 rounded up to a multiple of 8 entries per chunk, holds at
  * most 131072 entries.  That is up to 1,015,808 slots at n_experts = 256,
