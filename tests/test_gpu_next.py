@@ -369,6 +369,43 @@ def test_index_few_expert_path(s, k, e, dtype):
     _check_fused(ids, 0, 0, e)
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_index_random_shapes_around_the_few_expert_limits(seed):
+    """Seeded random inputs on both sides of the few-expert pass's limits
+    (experts 1-17, 1 to 40,000 slots, top_k 1-8), int32 and int64 maps,
+    uniform, skewed and garbage ids, separate and one-call forms with random
+    counts and scale alignments: every index output against the oracle."""
+    g = np.random.default_rng(4200 + seed)
+    for c in range(50):
+        e = int(g.choice([1, 2, 3, 5, 7, 8, 9, 12, 15, 16, 17]))
+        k = int(g.choice([1, 2, 3, 4, 6, 8]))
+        s = int(g.choice([g.integers(1, 2049), g.integers(2049, 16385), g.integers(16385, 32770),
+                          g.integers(32769, 40000)]))
+        n = max(1, s // k)
+        dt = np.int64 if g.random() < 0.3 else np.int32
+        kind = str(g.choice(["uniform", "skew", "garbage"]))
+        if kind == "uniform":
+            ids = g.integers(0, e, size=(n, k))
+        elif kind == "skew":
+            ids = np.minimum(g.geometric(0.5, size=(n, k)) - 1, e - 1)
+        else:
+            pool = [-1, -7, e, e + 3] + list(range(e)) + ([2 ** 33 + 1, -(2 ** 40)] if dt == np.int64 else [])
+            ids = g.choice(np.array(pool, np.int64), size=(n, k))
+        ids = ids.astype(dt)
+        real = int(g.choice([n, n - 1, 0, int(g.integers(0, n + 1)), n + 5]))
+        align = int(g.choice([1, 16, 128]))
+        print(f"[parity] few-expert sweep seed={seed} case={c}: n={n} k={k} e={e} {np.dtype(dt).name} {kind} "
+              f"real={real}", flush=True)
+        if g.random() < 0.5:
+            _check_fused(ids, real, 0, e, align)
+        else:
+            idx = _indices(torch.from_numpy(ids).to(DEV).view(-1), e, align)
+            ref = oracle.create_indices(ids, e, scales_align=align)
+            check_indices(idx, ref)
+            np.testing.assert_array_equal(u32(idx["scales_offset"]), ref["scales_offset"])
+            assert mod.index_workspace_error(idx["workspace"]) == 0
+
+
 @pytest.mark.parametrize("s, e", [(32768, 8), (16384, 16)])
 def test_index_few_expert_path_one_expert(s, e):
     """Every slot on one expert: the largest counts the pass keeps per wave."""
