@@ -51,6 +51,13 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 #define MOE_LOOKBACK_WINDOW 4
 #endif
 constexpr int kLookbackWindow = MOE_LOOKBACK_WINDOW;
+// Up to this many buckets (5 per lane), wave 0 alone scans the bucket
+// totals and writes the CSR outputs, with no barrier, while the other waves
+// go on; more buckets take the block-wide scan.
+#ifndef MOE_IDX_WAVE_FINALIZE_MAX_BUCKETS
+#define MOE_IDX_WAVE_FINALIZE_MAX_BUCKETS 320
+#endif
+constexpr int kWaveFinalizeMaxBuckets = MOE_IDX_WAVE_FINALIZE_MAX_BUCKETS;
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
@@ -235,14 +242,16 @@ __device__ void wave_scatter(const WaveTile<R>& tile, uint32_t n_experts, const 
 // Block-wide: from per-bucket totals tot[0..E] (LDS) write the bucket starts
 // base[0..E] (exclusive scan, base[E] = V) and, when `outputs` is set, the
 // compacted CSR outputs; with soff given, also the aligned offsets
-// (exclusive scan over active experts of their counts rounded up to `align`).
+// (exclusive scan over active experts of their counts rounded up to `align`);
+// with add_to given, add_to[b] += base[b] as well.  T = kWave: called by
+// wave 0 alone, with no barrier, so that the other waves can go on.
 template <int T>
 __device__ void finalize_counts(const uint32_t* tot, uint32_t n_experts, uint32_t* base,
                                 uint32_t* __restrict__ esi, int32_t* __restrict__ expert_ids,
                                 uint32_t* __restrict__ stats, uint32_t* __restrict__ soff,
-                                uint32_t align, bool outputs = true) {
+                                uint32_t align, bool outputs = true, uint32_t* add_to = nullptr) {
   constexpr int kWaves = T / kWave;
-  __shared__ uint32_t part[4 * kWaves];
+  __shared__ uint32_t part[kWaves > 1 ? 4 * kWaves : 1];
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
   const int nb = int(n_experts) + 1;
   const int ipt = (nb + T - 1) / T;
@@ -265,31 +274,39 @@ __device__ void finalize_counts(const uint32_t* tot, uint32_t n_experts, uint32_
   const uint32_t in_act = wave_inclusive_sum(s_act);
   const uint32_t in_al = wave_inclusive_sum(s_al);
   const uint32_t w_max = wave_max(s_max);
-  if (lane == kWave - 1) {
-    part[wave] = in_tot;
-    part[kWaves + wave] = in_act;
-    part[2 * kWaves + wave] = w_max;
-    part[3 * kWaves + wave] = in_al;
-  }
-  __syncthreads();
   uint32_t p_tot = in_tot - s_tot, p_act = in_act - s_act, p_al = in_al - s_al;
   uint32_t all_tot = 0, all_act = 0, all_max = 0, all_al = 0;
-  for (int w = 0; w < kWaves; ++w) {
-    if (w < wave) {
-      p_tot += part[w];
-      p_act += part[kWaves + w];
-      p_al += part[3 * kWaves + w];
+  if constexpr (kWaves == 1) {
+    all_tot = __builtin_amdgcn_readlane(in_tot, kWave - 1);
+    all_act = __builtin_amdgcn_readlane(in_act, kWave - 1);
+    all_max = w_max;
+    all_al = __builtin_amdgcn_readlane(in_al, kWave - 1);
+  } else {
+    if (lane == kWave - 1) {
+      part[wave] = in_tot;
+      part[kWaves + wave] = in_act;
+      part[2 * kWaves + wave] = w_max;
+      part[3 * kWaves + wave] = in_al;
     }
-    all_tot += part[w];
-    all_act += part[kWaves + w];
-    all_max = max(all_max, part[2 * kWaves + w]);
-    all_al += part[3 * kWaves + w];
+    __syncthreads();
+    for (int w = 0; w < kWaves; ++w) {
+      if (w < wave) {
+        p_tot += part[w];
+        p_act += part[kWaves + w];
+        p_al += part[3 * kWaves + w];
+      }
+      all_tot += part[w];
+      all_act += part[kWaves + w];
+      all_max = max(all_max, part[2 * kWaves + w]);
+      all_al += part[3 * kWaves + w];
+    }
   }
   for (int q = 0; q < ipt; ++q) {
     const int b = b0 + q;
     if (b < nb) {
       const uint32_t v = tot[b];
       base[b] = p_tot;
+      if (add_to != nullptr) add_to[b] += p_tot;
       if (outputs && b < int(n_experts) && v > 0) {
         expert_ids[p_act] = b;
         esi[p_act] = p_tot;
@@ -375,7 +392,11 @@ __global__ __launch_bounds__(T) void k_index_one(
     hist[b] = t;
   }
   __syncthreads();
-  finalize_counts<T>(hist, n_experts, base, esi, expert_ids, stats, soff, align);
+  if (nb <= kWaveFinalizeMaxBuckets) {
+    if (threadIdx.x < kWave) finalize_counts<kWave>(hist, n_experts, base, esi, expert_ids, stats, soff, align);
+  } else {
+    finalize_counts<T>(hist, n_experts, base, esi, expert_ids, stats, soff, align);
+  }
   __syncthreads();
   wave_scatter<false, R, T>(tile, n_experts, base, whist, teo, restore, n_slots);
 }
@@ -563,14 +584,18 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scatter_sum(
     }
   }
   __syncthreads();
-  // every workgroup scans the totals for the bucket starts; chunk 0 also
-  // writes the CSR outputs
-  finalize_counts<kIdxThreads>(tot, n_experts, base, esi, expert_ids, stats, soff, align, c == 0);
+  // every workgroup scans the totals for the bucket starts (chunk 0 also
+  // writes the CSR outputs) and adds them to its offsets; with few enough
+  // buckets wave 0 does it alone while the other waves rank their keys
+  if (nb <= kWaveFinalizeMaxBuckets) {
+    if (threadIdx.x < kWave)
+      finalize_counts<kWave>(tot, n_experts, base, esi, expert_ids, stats, soff, align, c == 0, off);
+  } else {
+    finalize_counts<kIdxThreads>(tot, n_experts, base, esi, expert_ids, stats, soff, align, c == 0, off);
+  }
   WaveTile<R> tile;
   wave_keys(id, static_cast<IdT*>(nullptr), n_slots, begin, n_experts, tile, n_slots);
   wave_count_keys(n_experts, nbits, whist, tile);
-  __syncthreads();
-  for (int b = threadIdx.x; b < nb; b += kIdxThreads) off[b] += base[b];
   __syncthreads();
   wave_scatter<false, R, kIdxThreads>(tile, n_experts, off, whist, teo, restore, n_slots);
 }
@@ -585,11 +610,13 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scatter_sum(
 // groups j < c*R lie in the chunks before chunk c.  Only routed slots are
 // counted; the unrouted bucket gets what they leave, of all slots (totals)
 // and of the c*R*kIdxThreads slots before the chunk (its offset).  The
-// chunk's own ids are loaded once more in the layout of the scatter, which
-// then follows as in k_index_scatter_sum.  Padding slots (the one-call mask
-// + index) are unrouted everywhere; only the owning chunk writes -1 into
-// them, and the other workgroups, which may read either value, never look
-// at it.  n_slots < 2^31 here, so slot indices are 32-bit.
+// chunk's own ids are loaded once more in the layout of the scatter.  With
+// at most 17 buckets, wave 0 alone scans the totals into the chunk's starts
+// (and in chunk 0 writes the CSR outputs) while the other waves rank their
+// keys; then the scatter follows as in k_index_scatter_sum.  Padding slots
+// (the one-call mask + index) are unrouted everywhere; only the owning chunk
+// writes -1 into them, and the other workgroups, which may read either
+// value, never look at it.  n_slots < 2^31 here, so slot indices are 32-bit.
 template <typename IdT, int R, int NB, int J>
 __global__ __launch_bounds__(kIdxThreads) void k_index_few(
     const IdT* ids, int64_t n_slots, uint32_t n_experts, int nbits, int n_chunks,
@@ -695,14 +722,13 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_few(
       tot[lane] = t;
       off[lane] = p;
     }
+    // the chunk's starts and, in chunk 0, the CSR outputs, by this wave alone
+    // while the other waves go on to their keys
+    finalize_counts<kWave>(tot, n_experts, base, esi, expert_ids, stats, soff, align, c == 0, off);
   }
-  __syncthreads();
-  finalize_counts<kIdxThreads>(tot, n_experts, base, esi, expert_ids, stats, soff, align, c == 0);
   WaveTile<R> tile;
   wave_keys(own, wmap, n_slots, begin, n_experts, tile, pad_from);
   wave_count_keys(n_experts, nbits, whist, tile);
-  __syncthreads();
-  for (int b = tid; b < nb; b += kIdxThreads) off[b] += base[b];
   __syncthreads();
   wave_scatter<false, R, kIdxThreads>(tile, n_experts, off, whist, teo, restore, n_slots);
 }
