@@ -32,13 +32,25 @@ namespace {
 #ifndef MOE_MXFP4_QUAD_UNITS
 #define MOE_MXFP4_QUAD_UNITS 2
 #endif
-// Cache policy (measured on MI355X): plain loads of x; non-temporal stores
-// for the separate payload rows, which are 128-byte aligned.
+// Cache policy (measured on MI355X): plain loads of x; for the separate
+// payload rows (128-byte aligned), plain stores for outputs of
+// [MOE_MXFP4_PLAIN_MIN_BYTES, MOE_MXFP4_PLAIN_MAX_BYTES), which the Infinity
+// Cache absorbs (a 36 MB output's pipeline 2.5% faster), and the
+// MOE_MXFP4_NT_STORE policy otherwise: non-temporal, since a 125 MB output
+// then leaves the next kernel more dirty lines to drain (its pipeline 0.9%
+// slower with plain stores), a 1.87 GB one took 4.5% longer, and the
+// latency-bound small outputs gain nothing (the same time on 8 MB).
 #ifndef MOE_MXFP4_NT_LOAD
 #define MOE_MXFP4_NT_LOAD 0
 #endif
 #ifndef MOE_MXFP4_NT_STORE
 #define MOE_MXFP4_NT_STORE 1
+#endif
+#ifndef MOE_MXFP4_PLAIN_MIN_BYTES
+#define MOE_MXFP4_PLAIN_MIN_BYTES (int64_t(16) << 20)
+#endif
+#ifndef MOE_MXFP4_PLAIN_MAX_BYTES
+#define MOE_MXFP4_PLAIN_MAX_BYTES (int64_t(64) << 20)
 #endif
 // Packed rows (17 bytes per block) are not 128-byte aligned, so adjacent
 // rows share cache lines; plain stores let the caches merge those lines.
@@ -118,8 +130,9 @@ __device__ __forceinline__ uint32_t words_amax(const uint32_t* w) {
 // 0.  kPacked: one row of 17*nblk bytes per slot, the 16*nblk payload bytes
 // first and the nblk scale bytes after them (the launcher checks
 // 17*nblk % 16 == 0, i.e. hidden % 512 == 0).  kEager (K > 0 only): each
-// lane's first block of x is requested before the positions.
-template <int K, bool kEven, bool kPacked, bool kEager>
+// lane's first block of x is requested before the positions.  kNtStore:
+// non-temporal payload stores (separate rows).
+template <int K, bool kEven, bool kPacked, bool kEager, bool kNtStore>
 __global__ __launch_bounds__(kMxThreads) void k_dispatch_mxfp4(
     const u32x4* __restrict__ x, int64_t n_rows, int h16, int top_k,
     const uint32_t* __restrict__ restore, uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
@@ -186,7 +199,7 @@ __global__ __launch_bounds__(kMxThreads) void k_dispatch_mxfp4(
           store_vec<MOE_MXFP4_PACKED_NT_STORE>(reinterpret_cast<u32x4*>(row) + b, pv);
           row[int64_t(nblk) * 16 + b] = sbyte;
         } else {
-          store_vec<MOE_MXFP4_NT_STORE>(reinterpret_cast<u32x4*>(q) + p * nblk + b, pv);
+          store_vec<kNtStore>(reinterpret_cast<u32x4*>(q) + p * nblk + b, pv);
           scales[p * nblk + b] = sbyte;
         }
       }
@@ -278,15 +291,22 @@ struct LaunchMxfp4 {
     }
     const RowSplit rs = row_split(n_rows, h16 / 4, kMxThreads / 2);
     const dim3 grid(row_grid(n_rows * rs.split)), block(kMxThreads);
+    const bool plain =
+        out_bytes >= double(MOE_MXFP4_PLAIN_MIN_BYTES) && out_bytes < double(MOE_MXFP4_PLAIN_MAX_BYTES);
+    constexpr bool kNt = MOE_MXFP4_NT_STORE != 0;
+#define MOE_MXFP4_GO(EAGER, NT)                                                                     \
+  hipLaunchKernelGGL((k_dispatch_mxfp4<K, kEven, kPacked, EAGER, NT>), grid, block, 0, s, x, n_rows, \
+                     h16, top_k, restore, q, scales, limit, rs)
     if constexpr (K > 0) {
       if (out_bytes >= double(MOE_MXFP4_EAGER_MIN_BYTES) && out_bytes < double(MOE_MXFP4_EAGER_MAX_BYTES)) {
-        hipLaunchKernelGGL((k_dispatch_mxfp4<K, kEven, kPacked, true>), grid, block, 0, s, x, n_rows,
-                           h16, top_k, restore, q, scales, limit, rs);
+        if (plain) MOE_MXFP4_GO(true, false);
+        else MOE_MXFP4_GO(true, kNt);
         return hipGetLastError();
       }
     }
-    hipLaunchKernelGGL((k_dispatch_mxfp4<K, kEven, kPacked, false>), grid, block, 0, s, x, n_rows, h16,
-                       top_k, restore, q, scales, limit, rs);
+    if (plain) MOE_MXFP4_GO(false, false);
+    else MOE_MXFP4_GO(false, kNt);
+#undef MOE_MXFP4_GO
     return hipGetLastError();
   }
   static hipError_t run(const u32x4* x, int64_t n_rows, int h16, int top_k, const uint32_t* restore,

@@ -638,31 +638,44 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_few(
   const int64_t begin = int64_t(c) * kChunkSlots;
   IdT own[R];
   wave_load_ids<false>(ids, n_slots, begin, own);
-  // all J groups' loads in flight together, each id reduced to its counted
-  // key at once (an expert, or kSent for the unrouted, padding and past the
-  // last slot) so that 32 groups of 64-bit ids need no more registers than
-  // 32-bit ones; groups past the last slot load the last slot again, in
-  // bounds
-  uint32_t key[J];
+  // all J groups' ids requested together through a bounds-checked buffer
+  // resource, so that no load needs a clamp: a slot past the last reads 0
+  // and is not counted.  Slot of group j: first(j) + lane_base.  64-bit ids
+  // are reduced to 32 bits at once (kSent when not an expert), so that 32
+  // groups of them need no more registers than 32-bit ones.
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<IdT*>(ids), 0, int(n32 * sizeof(IdT)), 0x00020000);
+  const uint32_t lane_base = uint32_t(wave * R) * kWave + lane;
+  uint32_t idv[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    const uint32_t i = uint32_t(j / R) * kChunkSlots + uint32_t(wave * R + j % R) * kWave + lane;
-    const uint32_t b = bucket_of(ids[i < n32 ? i : n32 - 1], n_experts);
-    key[j] = (i < pad32 && b < n_experts) ? b : kSent;  // pad32 <= n32
+    const uint32_t first = uint32_t(j / R) * kChunkSlots + uint32_t(j % R) * kWave;
+    const int voff = int((first + lane_base) * sizeof(IdT));
+    if constexpr (sizeof(IdT) == 4) {
+      idv[j] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, 0, 0);
+    } else {
+      const uint64_t id = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff, 0, 0));
+      idv[j] = id < uint64_t(n_experts) ? uint32_t(id) : kSent;
+    }
   }
   const int n_groups = n_chunks * R, g_own = c * R;
   // per lane, byte e of cnt[h] counts the lane's slots of expert 8h + e (at
   // most J <= 32 per byte); snap holds the counts of the groups before the
-  // chunk, a prefix of the loop
+  // chunk, a prefix of the loop.  A slot counts when it lies before pad32
+  // (padding and past the last slot do not) and its id is an expert.
   constexpr int H = NB / 8;
   uint64_t cnt[H] = {}, snap[H] = {};
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     if (j < n_groups) {  // the same for the whole workgroup
+      const uint32_t first = uint32_t(j / R) * kChunkSlots + uint32_t(j % R) * kWave;
+      const uint32_t bound = pad32 > first ? pad32 - first : 0u;  // lane_base < bound: before pad32
+      const bool counted = lane_base < bound && idv[j] < n_experts;
+      const uint32_t sh = (idv[j] & 7u) * 8u;
 #pragma unroll
       for (int h = 0; h < H; ++h) {
-        const uint32_t kh = key[j] - 8u * h;
-        cnt[h] += uint64_t(kh < 8u ? 1u : 0u) << ((kh & 7u) * 8u);
+        const bool in_h = H == 1 ? counted : (counted && (idv[j] >> 3) == uint32_t(h));
+        cnt[h] += uint64_t(in_h ? 1u : 0u) << sh;
       }
       if (j + 1 == g_own) {
 #pragma unroll
