@@ -643,6 +643,8 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_few(
   // and is not counted.  Slot of group j: first(j) + lane_base.  64-bit ids
   // are reduced to 32 bits at once (kSent when not an expert), so that 32
   // groups of them need no more registers than 32-bit ones.
+  // last resource word 0x00020000: 32-bit data format (bits 15-18 = 4), no
+  // swizzle, no index stride; a raw load at or past the size returns 0
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<IdT*>(ids), 0, int(n32 * sizeof(IdT)), 0x00020000);
   const uint32_t lane_base = uint32_t(wave * R) * kWave + lane;
