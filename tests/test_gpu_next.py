@@ -253,10 +253,12 @@ def test_combine_epilogue_whole_rows_sampled():
     np.testing.assert_array_equal(u16(out[torch.from_numpy(tok).to(DEV)]), want)
 
 
-def test_combine_epilogue_matches_combine_at_identity():
-    w = workloads.WORKLOADS[3]
-    ids, wts, real = workloads.make_routing(w, 3)
-    x, y = workloads.make_dense(w, 3, DEV)
+@pytest.mark.parametrize("cfg", [3, 1])   # decode; mixtral_prefill, whose y and output take plain stores
+def test_combine_epilogue_matches_combine_at_identity(cfg):
+    w = workloads.WORKLOADS[cfg]
+    ids, wts, real = workloads.make_routing(w, cfg)
+    x, y = workloads.make_dense(w, cfg, DEV)
+    print(f"[parity] combine epilogue at identity and with a residual: {w.name}", flush=True)
     m = oracle.mask_routing_padding(ids, real)
     ref = oracle.create_indices(m, w.n_experts)
     restore = torch.from_numpy(ref["restore_token_order"].view(np.int32)).to(DEV).view(torch.uint32)
