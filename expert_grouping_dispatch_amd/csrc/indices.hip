@@ -70,7 +70,7 @@ __device__ __forceinline__ uint32_t bucket_of(int64_t id, uint32_t n_experts) {
 }
 
 __device__ __forceinline__ bool is_leader(uint64_t peers) {
-  return peers != 0 && __builtin_ctzll(peers) == __lane_id();
+  return peers != 0 && __builtin_ctzll(peers) == int(__lane_id());
 }
 
 // First slot of the padding rows to mask (n_slots when nothing is masked):
@@ -405,7 +405,7 @@ __global__ __launch_bounds__(T) void k_index_one(
 // ticket) CSR outputs; the scatter follows in k_index_scatter.
 template <typename IdT, int R>
 __global__ __launch_bounds__(kIdxThreads) void k_index_hist(
-    const IdT* ids, int64_t n_slots, uint32_t n_experts, int nbits,
+    const IdT* ids, int64_t n_slots, uint32_t n_experts, int /*nbits*/,
     int64_t n_chunks, IndexWorkspace ws, uint32_t* __restrict__ esi,
     int32_t* __restrict__ expert_ids, uint32_t* __restrict__ stats, uint32_t* __restrict__ soff,
     uint32_t align, PadMask pad, IdT* wmap) {
