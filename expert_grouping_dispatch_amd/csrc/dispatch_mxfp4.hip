@@ -22,7 +22,15 @@ namespace {
 // Outputs (payload and scales) of at least MOE_MXFP4_QUAD_MIN_BYTES with
 // top_k <= 8 take the four-lanes-per-block kernel, whose workgroups have at
 // most MOE_MXFP4_QUAD_THREADS lanes, each loading MOE_MXFP4_QUAD_UNITS
-// 16-byte quarters of blocks per step.
+// 16-byte quarters of blocks per step.  It loads x non-temporally when x
+// holds at least MOE_MXFP4_QUAD_NT_LOAD_MIN_BYTES, more than the 256 MB
+// Infinity Cache keeps for the next reader.  Measured on MI355X with
+// 7168-wide rows and top_k 8: on a 2.75 GB output (x 939 MB), one quarter
+// per step and non-temporal loads take 0.48 ms in the pipeline against
+// 0.53 ms with two quarters and plain loads (each change alone gains about
+// half of that); non-temporal loads also win on x of 352 and 470 MB (2% and
+// 3%) but lose on x of 176 and 235 MB (0.105 ms against 0.083 ms, 0.138 ms
+// against 0.109 ms), which stays in that cache between calls.
 #ifndef MOE_MXFP4_QUAD_MIN_BYTES
 #define MOE_MXFP4_QUAD_MIN_BYTES (int64_t(256) << 20)
 #endif
@@ -30,10 +38,13 @@ namespace {
 #define MOE_MXFP4_QUAD_THREADS 512
 #endif
 #ifndef MOE_MXFP4_QUAD_UNITS
-#define MOE_MXFP4_QUAD_UNITS 2
+#define MOE_MXFP4_QUAD_UNITS 1
 #endif
-// Cache policy (measured on MI355X): plain loads of x; for the separate
-// payload rows (128-byte aligned), plain stores for outputs of
+#ifndef MOE_MXFP4_QUAD_NT_LOAD_MIN_BYTES
+#define MOE_MXFP4_QUAD_NT_LOAD_MIN_BYTES (int64_t(256) << 20)
+#endif
+// Cache policy of k_dispatch_mxfp4 (measured on MI355X): plain loads of x;
+// for the separate payload rows (128-byte aligned), plain stores for outputs of
 // [MOE_MXFP4_PLAIN_MIN_BYTES, MOE_MXFP4_PLAIN_MAX_BYTES), which the Infinity
 // Cache absorbs (a 36 MB output's pipeline 2.5% faster), and the
 // MOE_MXFP4_NT_STORE policy otherwise: non-temporal, since a 125 MB output
@@ -215,10 +226,10 @@ __global__ __launch_bounds__(kMxThreads) void k_dispatch_mxfp4(
 // maximum meets across the quad by DPP; each lane encodes its 8 elements
 // into one 32-bit word of payload and stores it to each routed position
 // (consecutive lanes write consecutive words); lane 0 of the quad stores the
-// scale byte.  kPacked as in k_dispatch_mxfp4.  The launcher makes `lanes`
-// a multiple of 4, and a row is a whole number of blocks, so the four lanes
-// of a quad are active together.
-template <int K, bool kEven, bool kPacked>
+// scale byte.  kPacked as in k_dispatch_mxfp4; kNtLoad: non-temporal loads
+// of x.  The launcher makes `lanes` a multiple of 4, and a row is a whole
+// number of blocks, so the four lanes of a quad are active together.
+template <int K, bool kEven, bool kPacked, bool kNtLoad>
 __global__ __launch_bounds__(kMxQuadThreads) void k_dispatch_mxfp4_quad(
     const u32x4* __restrict__ x, int h16, const uint32_t* __restrict__ restore,
     uint8_t* __restrict__ q, uint8_t* __restrict__ scales, uint32_t limit) {
@@ -240,7 +251,7 @@ __global__ __launch_bounds__(kMxQuadThreads) void k_dispatch_mxfp4_quad(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int unit = base + u * lanes + tid;
-      v[u] = unit < h16 ? load_vec<MOE_MXFP4_NT_LOAD>(src + unit) : u32x4{0u, 0u, 0u, 0u};
+      v[u] = unit < h16 ? load_vec<kNtLoad>(src + unit) : u32x4{0u, 0u, 0u, 0u};
     }
     uint32_t word[U], sbyte[U];
 #pragma unroll
@@ -284,8 +295,12 @@ struct LaunchMxfp4 {
         // the fewest quads that cover the row in kMxQuadUnits steps, at most kMxQuadThreads lanes
         const int quads = (h16 / 4 + kMxQuadUnits - 1) / kMxQuadUnits;
         const dim3 grid{uint32_t(n_rows)}, block{uint32_t(min(4 * quads, kMxQuadThreads))};
-        hipLaunchKernelGGL((k_dispatch_mxfp4_quad<K, kEven, kPacked>), grid, block, 0, s, x, h16, restore, q,
-                           scales, limit);
+        if (double(n_rows) * h16 * 16 >= double(MOE_MXFP4_QUAD_NT_LOAD_MIN_BYTES))
+          hipLaunchKernelGGL((k_dispatch_mxfp4_quad<K, kEven, kPacked, true>), grid, block, 0, s, x, h16,
+                             restore, q, scales, limit);
+        else
+          hipLaunchKernelGGL((k_dispatch_mxfp4_quad<K, kEven, kPacked, false>), grid, block, 0, s, x, h16,
+                             restore, q, scales, limit);
         return hipGetLastError();
       }
     }

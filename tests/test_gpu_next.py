@@ -149,7 +149,9 @@ def test_mxfp4_every_finite_value_wide_output(flags):
     top_k <= 8): every finite bf16 value under every block scale, in both
     scale modes and both layouts, bit-exact against the oracle.  8000 tokens
     tile the distinct rows of the exhaustive blocks, and each token goes to
-    all 8 experts (in a seeded order), so every row is written 8 times."""
+    all 8 experts (in a seeded order), so every row is written 8 times.  x
+    holds 131 MB, under the 256 MiB from which that kernel loads x
+    non-temporally, so this case takes its plain loads."""
     even, packed = bool(flags & mod.MXFP4_EVEN_SCALE), bool(flags & mod.MXFP4_PACKED_ROWS)
     xu = _every_finite_blocks(7 + int(even), 8192)
     n, k, e, h = 8000, 8, 8, 8192

@@ -137,7 +137,8 @@ def test_workload_full_size_every_row_mxfp4(cfg):
     oracle.mxfp4_quantize (row chunks on host threads) and compared with the
     rows at each of its routed positions.  deepseek_v3_prefill (125 MB of
     output) runs the eager one-lane-per-block kernel, the stress workload
-    (1.9 GB) the four-lanes-per-block kernel."""
+    (1.9 GB) the four-lanes-per-block kernel with non-temporal loads (x of
+    939 MB)."""
     w = workloads.WORKLOADS[cfg]
     ids, wts, real = workloads.make_routing(w, cfg)
     x, _ = workloads.make_dense(w, cfg, DEV, y_rows=1)
