@@ -178,32 +178,36 @@ def test_mxfp4_every_finite_value_wide_output(flags):
             assert torch.equal(sc[sl], want_s[src[sl]]), p0
 
 
-@pytest.mark.parametrize("n", [16383, 16384])
-def test_mxfp4_wide_output_at_the_non_temporal_load_switch(n):
+@pytest.mark.parametrize("n, flags", [(16383, 0), (16384, 0), (16384, 1), (16384, 2), (16384, 3)])
+def test_mxfp4_wide_output_at_the_non_temporal_load_switch(n, flags):
     """The four-lanes-per-block kernel loads x non-temporally once x holds
     256 MiB: 16,383 tokens of 8192 elements fall one row short (plain loads),
-    16,384 hold exactly 256 MiB (non-temporal loads).  Both outputs take that
-    kernel; every routed row of 400 sampled tokens, payload and scale bytes,
-    against the oracle."""
+    16,384 hold exactly 256 MiB (non-temporal loads, in both scale modes and
+    both layouts).  Every routed row of 400 sampled tokens, payload and scale
+    bytes, against the oracle."""
     k, e, h = 8, 64, 8192
+    even, packed = bool(flags & mod.MXFP4_EVEN_SCALE), bool(flags & mod.MXFP4_PACKED_ROWS)
     assert (n * h * 2 >= 256 << 20) == (n == 16384)
     assert n * k * (h // 32) * 17 >= 256 << 20
-    print(f"[parity] MXFP4 wide output at the load switch, n={n}", flush=True)
-    g = np.random.default_rng(500 + n)
+    print(f"[parity] MXFP4 wide output at the load switch, n={n} flags={flags}", flush=True)
+    g = np.random.default_rng(500 + n + 10 * flags)
     ids = np.argsort(g.random((n, e), dtype=np.float32), axis=1)[:, :k].astype(np.int32)
     ref = oracle.create_indices(ids, e)
-    gen = torch.Generator(device=DEV).manual_seed(600 + n)
+    gen = torch.Generator(device=DEV).manual_seed(600 + n + 10 * flags)
     x = (torch.randn((n, h), generator=gen, device=DEV) * 4).to(torch.bfloat16)
     restore = torch.from_numpy(ref["restore_token_order"].view(np.int32)).to(DEV).view(torch.uint32)
-    q, sc = mod.alloc_dispatch_mxfp4(n * k, h, DEV)
-    mod.moe_dispatch_mxfp4(x, k, restore, q, sc)
+    q, sc = mod.alloc_dispatch_mxfp4(n * k, h, DEV, packed=packed)
+    mod.moe_dispatch_mxfp4(x, k, restore, q, sc, flags=flags)
     torch.cuda.synchronize()
     toks = np.unique(np.concatenate([g.integers(0, n, size=398), [0, n - 1]]))
-    pq, ps = oracle.mxfp4_quantize(u16(x[torch.from_numpy(toks).to(DEV)]))
+    pq, ps = oracle.mxfp4_quantize(u16(x[torch.from_numpy(toks).to(DEV)]), even=even)
     pos = ref["restore_token_order"].reshape(n, k)[toks].astype(np.int64)   # k distinct experts: all routed
     d_pos = torch.from_numpy(pos.reshape(-1)).to(DEV)
-    np.testing.assert_array_equal(q[d_pos].cpu().numpy(), np.repeat(pq, k, axis=0))
-    np.testing.assert_array_equal(sc[d_pos].cpu().numpy(), np.repeat(ps, k, axis=0))
+    if packed:
+        np.testing.assert_array_equal(q[d_pos].cpu().numpy(), np.repeat(np.concatenate([pq, ps], axis=1), k, axis=0))
+    else:
+        np.testing.assert_array_equal(q[d_pos].cpu().numpy(), np.repeat(pq, k, axis=0))
+        np.testing.assert_array_equal(sc[d_pos].cpu().numpy(), np.repeat(ps, k, axis=0))
 
 
 def test_mxfp4_packed_full_size_sampled():
