@@ -58,6 +58,10 @@ constexpr int kLookbackWindow = MOE_LOOKBACK_WINDOW;
 #define MOE_IDX_WAVE_FINALIZE_MAX_BUCKETS 320
 #endif
 constexpr int kWaveFinalizeMaxBuckets = MOE_IDX_WAVE_FINALIZE_MAX_BUCKETS;
+constexpr int kWaveFinalizeIpt = (kWaveFinalizeMaxBuckets + kWave - 1) / kWave;  // buckets per lane
+static_assert(kWaveFinalizeMaxBuckets >= 1 && kWaveFinalizeMaxBuckets <= MOE_MAX_BUCKETS,
+              "the one-wave scan covers at most every bucket");
+static_assert(MOE_IDX_FEW_MAX_EXPERTS + 1 <= kWave, "the few-expert pass scans one bucket per lane");
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
@@ -244,8 +248,14 @@ __device__ void wave_scatter(const WaveTile<R>& tile, uint32_t n_experts, const 
 // compacted CSR outputs; with soff given, also the aligned offsets
 // (exclusive scan over active experts of their counts rounded up to `align`);
 // with add_to given, add_to[b] += base[b] as well.  T = kWave: called by
-// wave 0 alone, with no barrier, so that the other waves can go on.
-template <int T>
+// wave 0 alone, with no barrier, so that the other waves can go on.  Each
+// lane owns ipt = ceil((E+1)/T) consecutive buckets.  kMaxIpt > 0 bounds ipt
+// at compile time (a caller that passes less than the default guarantees
+// fewer buckets), and a lane's LDS reads are then issued together instead of
+// one after another; kMaxIpt = 0 keeps a loop over ipt, the default beyond 8
+// buckets a lane, where the unrolled form measured slower (1024 experts over
+// 64 lanes: 12.8 against 12.0 us).
+template <int T, int kMaxIpt = ((MOE_MAX_BUCKETS + T - 1) / T <= 8 ? (MOE_MAX_BUCKETS + T - 1) / T : 0)>
 __device__ void finalize_counts(const uint32_t* tot, uint32_t n_experts, uint32_t* base,
                                 uint32_t* __restrict__ esi, int32_t* __restrict__ expert_ids,
                                 uint32_t* __restrict__ stats, uint32_t* __restrict__ soff,
@@ -254,21 +264,32 @@ __device__ void finalize_counts(const uint32_t* tot, uint32_t n_experts, uint32_
   __shared__ uint32_t part[kWaves > 1 ? 4 * kWaves : 1];
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
   const int nb = int(n_experts) + 1;
-  const int ipt = (nb + T - 1) / T;
+  const int ipt = (nb + T - 1) / T;  // <= kMaxIpt
   const int b0 = tid * ipt;
   const bool want_soff = soff != nullptr;
+  constexpr int kV = kMaxIpt > 0 ? kMaxIpt : 1;
+  uint32_t v[kV];  // kMaxIpt > 0: the lane's bucket totals, 0 past its buckets
   uint32_t s_tot = 0, s_act = 0, s_max = 0, s_al = 0;
-  for (int q = 0; q < ipt; ++q) {
-    const int b = b0 + q;
-    if (b < nb) {
-      const uint32_t v = tot[b];
-      s_tot += v;
-      if (b < int(n_experts) && v > 0) {
-        s_act += 1u;
-        s_max = max(s_max, v);
-        if (want_soff) s_al += (v + align - 1) / align * align;
-      }
+  auto add_bucket = [&](int b, uint32_t x) {
+    s_tot += x;
+    if (b < int(n_experts) && x > 0) {
+      s_act += 1u;
+      s_max = max(s_max, x);
+      if (want_soff) s_al += (x + align - 1) / align * align;
     }
+  };
+  if constexpr (kMaxIpt > 0) {
+    // every read is issued (at a clamped address) so that none waits behind a branch
+#pragma unroll
+    for (int q = 0; q < kMaxIpt; ++q) {
+      const uint32_t x = tot[min(b0 + q, nb - 1)];
+      v[q] = (q < ipt && b0 + q < nb) ? x : 0u;
+    }
+#pragma unroll
+    for (int q = 0; q < kMaxIpt; ++q) add_bucket(b0 + q, v[q]);
+  } else {
+    for (int q = 0; q < ipt; ++q)
+      if (b0 + q < nb) add_bucket(b0 + q, tot[b0 + q]);
   }
   const uint32_t in_tot = wave_inclusive_sum(s_tot);
   const uint32_t in_act = wave_inclusive_sum(s_act);
@@ -301,22 +322,32 @@ __device__ void finalize_counts(const uint32_t* tot, uint32_t n_experts, uint32_
       all_al += part[3 * kWaves + w];
     }
   }
-  for (int q = 0; q < ipt; ++q) {
-    const int b = b0 + q;
-    if (b < nb) {
-      const uint32_t v = tot[b];
-      base[b] = p_tot;
-      if (add_to != nullptr) add_to[b] += p_tot;
-      if (outputs && b < int(n_experts) && v > 0) {
-        expert_ids[p_act] = b;
-        esi[p_act] = p_tot;
-        if (want_soff) {
-          soff[p_act] = p_al;
-          p_al += (v + align - 1) / align * align;
-        }
-        ++p_act;
+  // bucket b's start, its offsets and (chunk 0) its CSR entry; prev is add_to[b]
+  auto place_bucket = [&](int b, uint32_t x, uint32_t prev) {
+    base[b] = p_tot;
+    if (add_to != nullptr) add_to[b] = prev + p_tot;
+    if (outputs && b < int(n_experts) && x > 0) {
+      expert_ids[p_act] = b;
+      esi[p_act] = p_tot;
+      if (want_soff) {
+        soff[p_act] = p_al;
+        p_al += (x + align - 1) / align * align;
       }
-      p_tot += v;
+      ++p_act;
+    }
+    p_tot += x;
+  };
+  if constexpr (kMaxIpt > 0) {
+    uint32_t prev[kMaxIpt];
+#pragma unroll
+    for (int q = 0; q < kMaxIpt; ++q) prev[q] = add_to != nullptr ? add_to[min(b0 + q, nb - 1)] : 0u;
+#pragma unroll
+    for (int q = 0; q < kMaxIpt; ++q)
+      if (q < ipt && b0 + q < nb) place_bucket(b0 + q, v[q], prev[q]);
+  } else {
+    for (int q = 0; q < ipt; ++q) {
+      const int b = b0 + q;
+      if (b < nb) place_bucket(b, tot[b], add_to != nullptr ? add_to[b] : 0u);
     }
   }
   if (!outputs) return;
@@ -393,7 +424,8 @@ __global__ __launch_bounds__(T) void k_index_one(
   }
   __syncthreads();
   if (nb <= kWaveFinalizeMaxBuckets) {
-    if (threadIdx.x < kWave) finalize_counts<kWave>(hist, n_experts, base, esi, expert_ids, stats, soff, align);
+    if (threadIdx.x < kWave)
+      finalize_counts<kWave, kWaveFinalizeIpt>(hist, n_experts, base, esi, expert_ids, stats, soff, align);
   } else {
     finalize_counts<T>(hist, n_experts, base, esi, expert_ids, stats, soff, align);
   }
@@ -589,7 +621,8 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_scatter_sum(
   // buckets wave 0 does it alone while the other waves rank their keys
   if (nb <= kWaveFinalizeMaxBuckets) {
     if (threadIdx.x < kWave)
-      finalize_counts<kWave>(tot, n_experts, base, esi, expert_ids, stats, soff, align, c == 0, off);
+      finalize_counts<kWave, kWaveFinalizeIpt>(tot, n_experts, base, esi, expert_ids, stats, soff, align, c == 0,
+                                               off);
   } else {
     finalize_counts<kIdxThreads>(tot, n_experts, base, esi, expert_ids, stats, soff, align, c == 0, off);
   }
@@ -739,7 +772,7 @@ __global__ __launch_bounds__(kIdxThreads) void k_index_few(
     }
     // the chunk's starts and, in chunk 0, the CSR outputs, by this wave alone
     // while the other waves go on to their keys
-    finalize_counts<kWave>(tot, n_experts, base, esi, expert_ids, stats, soff, align, c == 0, off);
+    finalize_counts<kWave, 1>(tot, n_experts, base, esi, expert_ids, stats, soff, align, c == 0, off);
   }
   WaveTile<R> tile;
   wave_keys(own, wmap, n_slots, begin, n_experts, tile, pad_from);
