@@ -748,6 +748,29 @@ def test_index_count_table_row_padding(e, s):
     np.testing.assert_array_equal(u32(idx["scales_offset"]), ref["scales_offset"])
 
 
+# The scan of the bucket totals gives each lane ceil((E+1)/T) consecutive
+# buckets, with the reads unrolled to a compile-time bound that depends on
+# the path: E+1 on each side of 64, 128, 256 and 320 buckets (320 is the
+# most one wave scans alone), and 1024 experts, through the one-workgroup
+# pass at 64, 128, 256 and 1024 lanes (100, 200, 400 and 2000 slots) and the
+# count-table path at both chunk sizes.  Every index output and the aligned
+# offsets, bit-exact.
+@pytest.mark.parametrize("e", [63, 64, 127, 128, 255, 256, 319, 320, 1024])
+@pytest.mark.parametrize("s", [100, 200, 400, 2000, 9000, 70000])
+def test_index_scan_buckets_per_lane(e, s):
+    g = np.random.default_rng(e * 11 + s)
+    ids = g.integers(-1, e + 1, size=(s, 1)).astype(np.int32)
+    print(f"[parity] bucket scan: S={s} E={e}", flush=True)
+    d = torch.from_numpy(ids.reshape(-1)).to(DEV)
+    idx = mod.alloc_indices(s, e, DEV, scales_offset=True)
+    mod.moe_create_indices(d, e, idx["token_expert_order"], idx["expert_start_indices"], idx["restore_token_order"],
+                           idx["expert_ids"], idx["expert_usage_stats"], idx["workspace"], idx["scales_offset"], 16)
+    torch.cuda.synchronize()
+    ref = oracle.create_indices(ids, e, scales_align=16)
+    check_indices(idx, ref)
+    np.testing.assert_array_equal(u32(idx["scales_offset"]), ref["scales_offset"])
+
+
 def test_workspace_not_zero_filled_sets_error_word():
     """Misuse, forced from the host: the ticket word of the workspace is not
     zero, so the first chunks are never handed out and later chunks wait for
